@@ -1,0 +1,162 @@
+"""Grouped-query attention forward pass for MI355X (gfx950): Python binding of libgqa.so.
+
+The binding only checks tensors and passes pointers, sizes and the current HIP
+stream to the C ABI declared in include/gqa.h; every step of the computation
+runs in the library's HIP kernels. There is no fallback: if libgqa.so is not
+built, every call raises.
+
+    import grouped_query_attention_02_amd as gqa
+    o = gqa.prefill(q, k, v, causal=False, seqlens=lens)          # q [B,S,Hq,d]
+    o = gqa.decode(q, k_cache, v_cache, cache_lens=lens)           # q [B,Hq,d]
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+from ._lib import (GQA_DTYPE_BF16, GQA_DTYPE_F32, GQA_OK, GQAError, header_functions, load,
+                   status_string)
+
+__all__ = ["prefill", "decode", "decode_workspace_bytes", "decode_num_workgroups", "version",
+           "status_string", "GQAError", "load", "header_functions"]
+
+
+def version() -> int:
+    return int(load().gqa_version())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return GQA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return GQA_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _check(t, name, ndim, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _lens_arg(x, B, device, name):
+    torch = _torch()
+    if x is None:
+        return None, 0
+    if not isinstance(x, torch.Tensor):
+        x = torch.as_tensor(x, dtype=torch.int32)
+    if x.device != device:
+        x = x.to(device)
+    if x.dtype != torch.int32:
+        x = x.to(torch.int32)
+    x = x.contiguous()
+    if x.shape != (B,):
+        raise ValueError(f"{name} must have shape ({B},)")
+    return x, x.data_ptr()
+
+
+def _stream_ptr(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def prefill(q, k, v, *, causal: bool = False, softmax_scale: Optional[float] = None,
+            seqlens=None, return_lse: bool = False, out=None, lse_out=None):
+    """Attention of every query row over the valid keys of its sequence.
+
+    q [B, S, Hq, d], k/v [B, S, Hkv, d] (contiguous, same dtype: bfloat16 or float32,
+    on the GPU), seqlens int32 [B] valid key lengths or None. Returns o [B, S, Hq, d]
+    (and lse [B, Hq, S] float32 when return_lse).
+    """
+    torch = _torch()
+    _check(q, "q", 4)
+    _check(k, "k", 4, q.dtype)
+    _check(v, "v", 4, q.dtype)
+    B, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if tuple(k.shape) != (B, S, Hkv, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"k and v must be [B, S, Hkv, d] = [{B}, {S}, Hkv, {d}]")
+    if Hkv <= 0 or Hq % Hkv != 0:
+        raise ValueError(f"num_heads_q ({Hq}) must be divisible by num_heads_kv ({Hkv})")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", 4, q.dtype)
+    lse_ptr = 0
+    if return_lse:
+        if lse_out is None:
+            lse_out = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+        else:
+            _check(lse_out, "lse_out", 3, torch.float32)
+        lse_ptr = lse_out.data_ptr()
+    lens, lens_ptr = _lens_arg(seqlens, B, q.device, "seqlens")
+    st = load().gqa_prefill(_dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                            out.data_ptr(), lse_ptr or None, lens_ptr or None, B, S, Hq, Hkv, d,
+                            scale, int(bool(causal)), _stream_ptr(q.device))
+    if st != GQA_OK:
+        raise GQAError(st, "gqa_prefill")
+    return (out, lse_out) if return_lse else out
+
+
+def decode_workspace_bytes(B: int, Hq: int, Hkv: int, d: int, max_len: int,
+                           num_splits: int = 0) -> int:
+    return int(load().gqa_decode_workspace_bytes(B, Hq, Hkv, d, max_len, num_splits))
+
+
+def decode_num_workgroups(B: int, Hq: int, Hkv: int, max_len: int, num_splits: int = 0) -> int:
+    return int(load().gqa_decode_num_workgroups(B, Hq, Hkv, max_len, num_splits))
+
+
+def decode(q, k_cache, v_cache, cache_lens=None, *, softmax_scale: Optional[float] = None,
+           num_splits: int = 0, return_lse: bool = False, workspace=None, out=None,
+           lse_out=None):
+    """One query token per sequence over its KV cache.
+
+    q [B, Hq, d], k_cache/v_cache [B, Hkv, max_len, d] (bfloat16, contiguous, on the
+    GPU), cache_lens int32 [B] or None (= max_len). Returns o [B, Hq, d] (and lse
+    [B, Hq] float32 when return_lse). `workspace` (uint8 GPU tensor) is allocated
+    when not given.
+    """
+    torch = _torch()
+    _check(q, "q", 3)
+    _check(k_cache, "k_cache", 4, q.dtype)
+    _check(v_cache, "v_cache", 4, q.dtype)
+    B, Hq, d = q.shape
+    Hkv, max_len = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, Hkv, max_len, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache and v_cache must be [B, Hkv, max_len, d]")
+    if Hkv <= 0 or Hq % Hkv != 0:
+        raise ValueError(f"num_heads_q ({Hq}) must be divisible by num_heads_kv ({Hkv})")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    need = decode_workspace_bytes(B, Hq, Hkv, d, max_len, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", 3, q.dtype)
+    lse_ptr = 0
+    if return_lse:
+        if lse_out is None:
+            lse_out = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+        lse_ptr = lse_out.data_ptr()
+    lens, lens_ptr = _lens_arg(cache_lens, B, q.device, "cache_lens")
+    st = load().gqa_decode(_dtype_code(q), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                           lens_ptr or None, out.data_ptr(), lse_ptr or None, B, Hq, Hkv, d,
+                           max_len, scale, int(num_splits), workspace.data_ptr(),
+                           workspace.numel() * workspace.element_size(), _stream_ptr(q.device))
+    if st != GQA_OK:
+        raise GQAError(st, "gqa_decode")
+    return (out, lse_out) if return_lse else out

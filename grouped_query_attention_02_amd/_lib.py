@@ -1,0 +1,66 @@
+"""ctypes loader for libgqa.so (argument marshalling only)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgqa.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "gqa.h")
+
+GQA_OK = 0
+GQA_ERR_INVALID_ARG = 1
+GQA_ERR_UNSUPPORTED = 2
+GQA_ERR_WORKSPACE = 3
+GQA_ERR_HIP = 4
+GQA_DTYPE_F32 = 0
+GQA_DTYPE_BF16 = 1
+
+_lib = None
+
+
+class GQAError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+def header_functions():
+    """Names of every function the public header declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gqa_[a-z0-9_]+)\s*\(", text)))
+
+
+def load():
+    """Load libgqa.so from the package directory; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m grouped_query_attention_02_amd.build` "
+            "(there is no fallback path)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.gqa_version.argtypes = []
+    lib.gqa_version.restype = i32
+    lib.gqa_status_string.argtypes = [i32]
+    lib.gqa_status_string.restype = ctypes.c_char_p
+    lib.gqa_prefill.argtypes = [i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.gqa_prefill.restype = i32
+    lib.gqa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.gqa_decode_workspace_bytes.restype = sz
+    lib.gqa_decode_num_workgroups.argtypes = [i32, i32, i32, i32, i32]
+    lib.gqa_decode_num_workgroups.restype = i32
+    lib.gqa_decode.argtypes = [i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
+                               vp, sz, vp]
+    lib.gqa_decode.restype = i32
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().gqa_status_string(int(status)).decode()

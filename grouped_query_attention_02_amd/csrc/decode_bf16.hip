@@ -1,0 +1,433 @@
+// decode_bf16.hip - bf16 grouped-query attention decode over a ragged KV cache.
+//
+// One new query token per sequence reads every cached K/V row of its K/V head, so
+// decode is bound by HBM bandwidth, and with grouping each K/V row read serves all
+// g query heads of the group (azimuth.plus GQA digest, "the bottleneck" section and
+// the KV-cache size formula 2 x L x G x d_k x n).
+//
+// Work split (split-KV with a log-sum-exp merge; the pages' `num_splits` knob,
+// blog.gitcode.com "3个GQA核心优化技巧", section "阶段二：高级优化参数"):
+//   * unit u = (b, kvh, query block of <= 32 heads); unit u has T_u = ceil(L_b / 32)
+//     key tiles of 32 rows; all units' tiles are concatenated (T tiles in total);
+//   * workgroup w of W = min(launched, T) takes tiles [floor(w T / W), floor((w+1) T / W)),
+//     so every workgroup streams the same number of rows whatever the length mix,
+//     and a sequence is split into as many pieces as shares overlap it;
+//   * a workgroup covering a whole unit writes the final output; otherwise it writes
+//     a normalised fp32 partial and its LSE to slot (w + u) (w and u never both
+//     decrease along the tile order, so w + u is unique), and the combine kernel
+//     merges a unit's partials in workgroup order with weights exp(lse_s - max).
+// Inside a workgroup the 4 waves take the segment's tiles round-robin and merge
+// their running (max, sum, O) through LDS.
+//
+// Per 32-key tile, per wave (lane l: query l % 32 of the block, key half l / 32):
+//   S^T = K Q^T   (d/16) MFMA 32x32x16; K rows come straight from HBM as the A
+//                 operand (16 bytes per lane), Q^T stays in VGPRs;
+//   online softmax over the 32 keys (running max / running sum);
+//   O^T += V^T P^T  2 x (d/32) MFMA; each lane loads d/32 consecutive values of 8
+//                 keys (one full row per 32 lanes, coalesced), and byte permutes
+//                 build the V^T operand for output columns d = (d/32) * m + c.
+// Rows at or past L_b are never read.
+#include "gqa_device.h"
+#include "gqa_kernels.h"
+
+namespace gqa {
+namespace {
+
+constexpr int DC_WAVES = 4;
+constexpr int DC_THREADS = 64 * DC_WAVES;
+constexpr int DC_TILE = 32;
+
+__device__ __forceinline__ int clamp_len(const int32_t* lens, int b, int cap) {
+  if (!lens) return cap;
+  int L = lens[b];
+  return L < 0 ? 0 : (L > cap ? cap : L);
+}
+
+__device__ __forceinline__ int tiles_of(int L) { return (L + DC_TILE - 1) / DC_TILE; }
+
+// Sum of an int over the workgroup (all threads get the result).
+__device__ long long block_sum(long long v, long long* scratch) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) scratch[wave] = v;
+  __syncthreads();
+  long long t = 0;
+#pragma unroll
+  for (int w = 0; w < DC_WAVES; ++w) t += scratch[w];
+  return t;
+}
+
+// Tiles of sequences [0, B) (per K/V unit of one sequence) and of [0, b_end).
+__device__ void tile_prefix(const int32_t* lens, int B, int cap, int b_end, long long* total,
+                            long long* before, long long* scratch) {
+  long long tot = 0, bef = 0;
+  for (int base = 0; base < B; base += DC_THREADS) {
+    const int bb = base + threadIdx.x;
+    const long long tb = bb < B ? tiles_of(clamp_len(lens, bb, cap)) : 0;
+    tot += block_sum(tb, scratch);
+    bef += block_sum(bb < b_end ? tb : 0, scratch);
+  }
+  *total = tot;
+  *before = bef;
+}
+
+// First sequence whose tile range (in concatenated unit order) ends after tile t0,
+// and the first tile of that sequence.
+__device__ void find_seq(const int32_t* lens, int B, int cap, long long HU, long long t0,
+                         int* b_out, long long* start_out, long long* scratch) {
+  long long run = 0;  // tiles of sequences before this chunk
+  if (threadIdx.x == 0) {
+    scratch[DC_WAVES] = 0;
+    scratch[DC_WAVES + 1] = 0;
+  }
+  for (int base = 0; base < B; base += DC_THREADS) {
+    const int bb = base + threadIdx.x;
+    const long long tb = bb < B ? HU * tiles_of(clamp_len(lens, bb, cap)) : 0;
+    // inclusive scan of tb across the workgroup
+    long long x = tb;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const long long y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
+    }
+    __syncthreads();
+    if (lane == 63) scratch[wave] = x;
+    __syncthreads();
+    long long wave_off = 0;
+    for (int w = 0; w < wave; ++w) wave_off += scratch[w];
+    long long chunk_total = 0;
+#pragma unroll
+    for (int w = 0; w < DC_WAVES; ++w) chunk_total += scratch[w];
+    const long long incl = run + wave_off + x;  // tiles through sequence bb
+    const long long excl = incl - tb;
+    // the sequence containing tile t0: excl <= t0 < incl
+    const bool hit = bb < B && excl <= t0 && t0 < incl;
+    __syncthreads();
+    if (hit) {
+      scratch[DC_WAVES] = bb;
+      scratch[DC_WAVES + 1] = excl;
+    }
+    __syncthreads();
+    if (run + chunk_total > t0) break;  // uniform: the hit was in this chunk
+    run += chunk_total;
+  }
+  *b_out = (int)scratch[DC_WAVES];
+  *start_out = scratch[DC_WAVES + 1];
+}
+
+template <int D>
+struct DcLayout {
+  static constexpr int OSTR = D + 4;  // floats per query row of a wave's O in LDS
+  static constexpr int O_FLOATS = DC_WAVES * 32 * OSTR;
+};
+
+template <int D>
+__global__ __launch_bounds__(DC_THREADS, 2) void decode_split_kernel(DecodeParams p) {
+  constexpr int DPL = D / 32;  // output columns per lane in the V^T operand
+  using Lay = DcLayout<D>;
+  extern __shared__ __attribute__((aligned(16))) float dsm[];
+  float* s_o = dsm;                        // [wave][32][OSTR]
+  float* s_m = dsm + Lay::O_FLOATS;        // [wave][32]
+  float* s_l = s_m + DC_WAVES * 32;        // [wave][32]
+  long long* scratch = reinterpret_cast<long long*>(s_l + DC_WAVES * 32);  // 8 entries
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+  const int w = blockIdx.x;
+  const int cap = p.max_len;
+  const long long HU = (long long)p.Hkv * p.nqb;
+  const float c = p.scale_log2;
+
+  long long T, unused;
+  tile_prefix(p.lens, p.B, cap, 0, &T, &unused, scratch);
+  T *= HU;
+  // Never more shares than tiles, so every share is non-empty and the shares
+  // overlapping a unit form one run of consecutive workgroups.
+  const long long W = T < p.n_wg ? T : p.n_wg;
+  if (w >= W) return;
+  const long long t_begin = (long long)w * T / W;
+  const long long t_end = (long long)(w + 1) * T / W;
+  if (t_begin >= t_end) return;
+
+  int b;
+  long long bstart;
+  find_seq(p.lens, p.B, cap, HU, t_begin, &b, &bstart, scratch);
+
+  const uint32_t flip = p.negate_q ? 0x80008000u : 0u;
+  long long t = t_begin;
+  while (t < t_end && b < p.B) {
+    const int Lb = clamp_len(p.lens, b, cap);
+    const int Tb = tiles_of(Lb);
+    const long long bend = bstart + HU * Tb;
+    if (Tb == 0 || t >= bend) {
+      bstart = bend;
+      ++b;
+      continue;
+    }
+    const int ui = (int)((t - bstart) / Tb);
+    const long long ustart = bstart + (long long)ui * Tb;
+    const int ta = (int)(t - ustart);
+    const int te = (int)(min(t_end, ustart + Tb) - ustart);
+    const int kvh = ui / p.nqb, qb = ui - kvh * p.nqb;
+    const int hbase = kvh * p.g + qb * 32;
+    const int nh = min(32, p.g - qb * 32);
+    const int u = (b * p.Hkv + kvh) * p.nqb + qb;
+
+    // Q^T (B operand): lane holds head hbase + l32, d = ks*16 + hh*8 .. +7.
+    bf16x8 qf[D / 16];
+    {
+      const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + ((size_t)b * p.Hq + hbase + l32) * D;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        u32x4 v = l32 < nh ? ldg16(qrow + ks * 16 + hh * 8) : zero_u32x4();
+        v[0] ^= flip; v[1] ^= flip; v[2] ^= flip; v[3] ^= flip;
+        qf[ks] = as_bf16x8(v);
+      }
+    }
+    const size_t cache_off = ((size_t)(b * p.Hkv + kvh) * cap) * D;
+    const uint16_t* kb_ = static_cast<const uint16_t*>(p.kc) + cache_off;
+    const uint16_t* vb_ = static_cast<const uint16_t*>(p.vc) + cache_off;
+
+    f32x16 oacc[DPL];
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) oacc[i] = zero16();
+    float m_run = -INFINITY, l_run = 0.f;
+
+    for (int tt = ta + wave; tt < te; tt += DC_WAVES) {
+      const int j0 = tt * DC_TILE;
+      // K rows (A operand): lane reads 16 bytes of row j0 + l32.
+      u32x4 kf[D / 16];
+      const int jk = j0 + l32;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks)
+        kf[ks] = jk < Lb ? ldg16(kb_ + (size_t)jk * D + ks * 16 + hh * 8) : zero_u32x4();
+      // V rows: for 16-key step ks2 and slot i, key j0 + 16ks2 + 8(i/4) + 4hh + (i%4);
+      // the lane reads DPL consecutive values starting at d = DPL * l32.
+      uint32_t vl[2][8][DPL / 2];
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int jv = j0 + 16 * ks2 + 8 * (i >> 2) + 4 * hh + (i & 3);
+          const uint16_t* src = vb_ + (size_t)jv * D + DPL * l32;
+          if constexpr (DPL == 4) {
+            const u32x2 x = jv < Lb ? ldg8(src) : u32x2{0u, 0u};
+            vl[ks2][i][0] = x[0];
+            vl[ks2][i][1] = x[1];
+          } else {
+            vl[ks2][i][0] = jv < Lb ? *reinterpret_cast<const uint32_t*>(src) : 0u;
+          }
+        }
+
+      f32x16 s = zero16();
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) s = mfma_bf16_32x32x16(as_bf16x8(kf[ks]), qf[ks], s);
+
+      const bool need_mask = j0 + DC_TILE > Lb;
+      if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = j0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (j >= Lb) s[r] = -INFINITY;
+        }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      mx = fmaxf(mx, xor32(mx));
+      const float m_new = fmaxf(m_run, mx);
+      if (wave_any(m_new > m_run)) {
+        const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_new) * c);
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < DPL; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+        m_run = m_new;
+      }
+      const float msc = (m_run == -INFINITY ? 0.f : m_run) * c;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pv = fast_exp2(fmaf(s[r], c, -msc));
+        if (need_mask) pv = (s[r] == -INFINITY) ? 0.f : pv;
+        s[r] = pv;
+        l_run += pv;
+      }
+
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+        const int r0 = 8 * ks2;
+        const bf16x8 pb = pack_bf16x8(s[r0 + 0], s[r0 + 1], s[r0 + 2], s[r0 + 3], s[r0 + 4],
+                                      s[r0 + 5], s[r0 + 6], s[r0 + 7]);
+#pragma unroll
+        for (int cc = 0; cc < DPL; ++cc) {
+          const int word = cc >> 1;       // which dword of the lane's DPL values
+          const bool upper = cc & 1;      // low or high bf16 of that dword
+          u32x4 a;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const uint32_t x0 = vl[ks2][2 * jj][word], x1 = vl[ks2][2 * jj + 1][word];
+            a[jj] = upper ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
+          }
+          oacc[cc] = mfma_bf16_32x32x16(as_bf16x8(a), pb, oacc[cc]);
+        }
+      }
+    }
+
+    // Merge the waves' running states through LDS.
+    const float l_tot = l_run + xor32(l_run);
+    if (hh == 0) {
+      s_m[wave * 32 + l32] = m_run;
+      s_l[wave * 32 + l32] = l_tot;
+    }
+#pragma unroll
+    for (int cc = 0; cc < DPL; ++cc)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int d = DPL * (8 * (r >> 2) + 4 * hh + (r & 3)) + cc;
+        s_o[(wave * 32 + l32) * Lay::OSTR + d] = oacc[cc][r];
+      }
+    __syncthreads();
+    {
+      const int n = tid >> 3;                 // query of the block
+      const int dseg = (tid & 7) * (D / 8);   // D/8 output columns per thread
+      float M = -INFINITY;
+#pragma unroll
+      for (int wv = 0; wv < DC_WAVES; ++wv) M = fmaxf(M, s_m[wv * 32 + n]);
+      float wgt[DC_WAVES];
+      float lsum = 0.f;
+#pragma unroll
+      for (int wv = 0; wv < DC_WAVES; ++wv) {
+        const float mw = s_m[wv * 32 + n];
+        wgt[wv] = (mw == -INFINITY) ? 0.f : fast_exp2((mw - M) * c);
+        lsum += wgt[wv] * s_l[wv * 32 + n];
+      }
+      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+      const float lse_v = lsum > 0.f ? M * p.scale_abs + logf(lsum) : -INFINITY;
+      if (n < nh) {
+        float val[D / 8];
+#pragma unroll
+        for (int dd = 0; dd < D / 8; ++dd) {
+          float acc = 0.f;
+#pragma unroll
+          for (int wv = 0; wv < DC_WAVES; ++wv)
+            acc += wgt[wv] * s_o[(wv * 32 + n) * Lay::OSTR + dseg + dd];
+          val[dd] = acc * inv;
+        }
+        if (ta == 0 && te == Tb) {
+          uint16_t* orow = static_cast<uint16_t*>(p.o) + ((size_t)b * p.Hq + hbase + n) * D + dseg;
+#pragma unroll
+          for (int q4 = 0; q4 < D / 64; ++q4) {
+            u32x4 wv4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wv4[e] = pack_bf16x2(val[8 * q4 + 2 * e], val[8 * q4 + 2 * e + 1]);
+            *reinterpret_cast<u32x4*>(orow + 8 * q4) = wv4;
+          }
+          if (p.lse && (tid & 7) == 0) p.lse[(size_t)b * p.Hq + hbase + n] = lse_v;
+        } else {
+          const size_t slot = (size_t)w + u;
+          float* dst = p.ws_o + (slot * 32 + n) * D + dseg;
+#pragma unroll
+          for (int q4 = 0; q4 < D / 32; ++q4) {
+            u32x4 wv4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wv4[e] = __float_as_uint(val[4 * q4 + e]);
+            *reinterpret_cast<u32x4*>(dst + 4 * q4) = wv4;
+          }
+          if ((tid & 7) == 0) p.ws_lse[slot * 32 + n] = lse_v;
+        }
+      }
+    }
+    __syncthreads();  // LDS is reused by the next segment
+    t = ustart + te;
+  }
+}
+
+// Merge the split partials of one unit (b, kvh, query block).
+template <int D>
+__global__ __launch_bounds__(DC_THREADS) void decode_combine_kernel(DecodeParams p) {
+  __shared__ long long scratch[DC_WAVES + 2];
+  const int u = blockIdx.x;
+  const int qb = u % p.nqb;
+  const int kvh = (u / p.nqb) % p.Hkv;
+  const int b = u / (p.nqb * p.Hkv);
+  const int cap = p.max_len;
+  const long long HU = (long long)p.Hkv * p.nqb;
+  long long T, before;
+  tile_prefix(p.lens, p.B, cap, b, &T, &before, scratch);
+  T *= HU;
+  const int Tb = tiles_of(clamp_len(p.lens, b, cap));
+  const int hbase = kvh * p.g + qb * 32;
+  const int nh = min(32, p.g - qb * 32);
+  uint16_t* obase = static_cast<uint16_t*>(p.o) + ((size_t)b * p.Hq + hbase) * D;
+
+  if (Tb == 0) {  // empty cache: O = 0, LSE = -inf
+    for (int idx = threadIdx.x; idx < nh * D; idx += DC_THREADS) obase[idx] = 0;
+    if (p.lse && threadIdx.x < nh) p.lse[(size_t)b * p.Hq + hbase + threadIdx.x] = -INFINITY;
+    return;
+  }
+  const long long W = T < p.n_wg ? T : p.n_wg;  // the split kernel's effective share count
+  const long long ustart = before * HU + (long long)(kvh * p.nqb + qb) * Tb;
+  const long long ulast = ustart + Tb - 1;
+  const int wa = (int)(((ustart + 1) * W - 1) / T);
+  const int wb = (int)(((ulast + 1) * W - 1) / T);
+  if (wa == wb) return;  // one workgroup covered the unit and wrote the output
+
+  for (int idx = threadIdx.x; idx < nh * (D / 4); idx += DC_THREADS) {
+    const int n = idx / (D / 4);
+    const int d0 = (idx - n * (D / 4)) * 4;
+    float M = -INFINITY;
+    for (int wv = wa; wv <= wb; ++wv) M = fmaxf(M, p.ws_lse[((size_t)wv + u) * 32 + n]);
+    float den = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int wv = wa; wv <= wb; ++wv) {
+      const size_t slot = (size_t)wv + u;
+      const float lw = p.ws_lse[slot * 32 + n];
+      const float e = (lw == -INFINITY) ? 0.f : fast_exp2((lw - M) * kLog2e);
+      den += e;
+      const u32x4 ov = ldg16(p.ws_o + (slot * 32 + n) * D + d0);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] += e * __uint_as_float(ov[k]);
+    }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    u32x2 o2;
+    o2[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    o2[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    *reinterpret_cast<u32x2*>(obase + (size_t)n * D + d0) = o2;
+    if (p.lse && d0 == 0)
+      p.lse[(size_t)b * p.Hq + hbase + n] = den > 0.f ? M + logf(den) : -INFINITY;
+  }
+}
+
+template <int D>
+hipError_t launch_d(const DecodeParams& p, bool need_combine, hipStream_t stream) {
+  using Lay = DcLayout<D>;
+  const size_t lds = (Lay::O_FLOATS + 2 * DC_WAVES * 32) * sizeof(float) +
+                     (DC_WAVES + 4) * sizeof(long long);
+  auto kern = decode_split_kernel<D>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(p.n_wg), dim3(DC_THREADS), lds, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess || !need_combine) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(p.n_units), dim3(DC_THREADS), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_bf16(const DecodeParams& p, bool need_combine, hipStream_t stream) {
+  switch (p.d) {
+    case 64: return launch_d<64>(p, need_combine, stream);
+    case 128: return launch_d<128>(p, need_combine, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace gqa

@@ -1,0 +1,164 @@
+// gqa_api.hip - C ABI of libgqa.so: argument validation, launch planning, dispatch.
+//
+// Every argument check runs on the host before anything touches the HIP runtime,
+// so invalid calls return a status code without a device present.
+#include <limits.h>
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gqa.h"
+#include "gqa_kernels.h"
+
+namespace {
+
+constexpr int kVersion = 10000;  // 1.0.0
+constexpr int kDecodeTile = 32;  // keys per decode tile
+constexpr int kDecodeAutoShares = 512;  // auto split: at least 2 workgroups per CU of a 256-CU GPU
+constexpr float kLog2e = 1.4426950408889634f;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_prefill_d(int dtype, int d) {
+  (void)dtype;
+  return d == 32 || d == 64 || d == 128;
+}
+
+bool supported_decode_d(int d) { return d == 64 || d == 128; }
+
+struct DecodePlan {
+  int nqb;
+  int n_units;
+  int n_wg;
+  size_t ws_bytes;
+  size_t ws_lse_offset;
+};
+
+// Shapes only; returns false for invalid arguments.
+bool plan_decode(int B, int Hq, int Hkv, int d, int max_len, int num_splits, DecodePlan* out) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_len <= 0 || num_splits < 0) return false;
+  if (Hq % Hkv != 0) return false;
+  const int g = Hq / Hkv;
+  const long long nqb = (g + 31) / 32;
+  const long long units = (long long)B * Hkv * nqb;
+  const long long max_tiles = (max_len + kDecodeTile - 1) / kDecodeTile;
+  long long wg;
+  if (num_splits == 0) {
+    wg = units > kDecodeAutoShares ? units : kDecodeAutoShares;
+  } else {
+    wg = (long long)num_splits * units;
+  }
+  if (wg > units * max_tiles) wg = units * max_tiles;  // never more shares than tiles
+  if (units > INT_MAX / 2 || wg > INT_MAX / 2) return false;
+  const long long slots = wg + units;
+  out->nqb = (int)nqb;
+  out->n_units = (int)units;
+  out->n_wg = (int)wg;
+  out->ws_lse_offset = (size_t)slots * 32 * d * sizeof(float);
+  out->ws_bytes = out->ws_lse_offset + (size_t)slots * 32 * sizeof(float);
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_version(void) { return kVersion; }
+
+const char* gqa_status_string(int status) {
+  switch (status) {
+    case GQA_OK: return "ok";
+    case GQA_ERR_INVALID_ARG: return "invalid argument";
+    case GQA_ERR_UNSUPPORTED: return "unsupported head size or dtype";
+    case GQA_ERR_WORKSPACE: return "decode workspace missing or too small";
+    case GQA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int gqa_prefill(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+                const int32_t* seqlens, int B, int S, int Hq, int Hkv, int d,
+                float softmax_scale, int causal, void* stream) {
+  if (B <= 0 || S <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return GQA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return GQA_ERR_INVALID_ARG;
+  if (!q || !k || !v || !o) return GQA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return GQA_ERR_INVALID_ARG;
+  if ((lse && ((uintptr_t)lse & 3u)) || (seqlens && ((uintptr_t)seqlens & 3u)))
+    return GQA_ERR_INVALID_ARG;
+  if (!isfinite(softmax_scale)) return GQA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return GQA_ERR_INVALID_ARG;
+  if (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16) return GQA_ERR_UNSUPPORTED;
+  if (!supported_prefill_d(dtype, d)) return GQA_ERR_UNSUPPORTED;
+  const int g = Hq / Hkv;
+  if ((long long)S * g > INT_MAX / 2 || (long long)B * S * Hq > (long long)INT_MAX * 64)
+    return GQA_ERR_INVALID_ARG;
+
+  gqa::PrefillParams p;
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse; p.seqlens = seqlens;
+  p.B = B; p.S = S; p.Hq = Hq; p.Hkv = Hkv; p.g = g; p.d = d;
+  p.scale_abs = fabsf(softmax_scale);
+  p.scale_log2 = p.scale_abs * kLog2e;
+  p.negate_q = softmax_scale < 0.f ? 1 : 0;
+  p.rows_per_wg = dtype == GQA_DTYPE_BF16 ? gqa::prefill_rows_per_wg_bf16()
+                                          : gqa::prefill_rows_per_wg_f32();
+  const long long rows = (long long)S * g;
+  const long long nrb = (rows + p.rows_per_wg - 1) / p.rows_per_wg;
+  const long long n_wg = nrb * B * Hkv;
+  if (n_wg > INT_MAX / 2) return GQA_ERR_INVALID_ARG;
+  p.nrb = (int)nrb;
+  p.n_wg = (int)n_wg;
+  p.per_xcd = (int)((n_wg + 7) / 8);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = dtype == GQA_DTYPE_BF16 ? gqa::launch_prefill_bf16(p, causal, s)
+                                         : gqa::launch_prefill_f32(p, causal, s);
+  return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+size_t gqa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_len, int num_splits) {
+  DecodePlan plan;
+  if (!plan_decode(B, Hq, Hkv, d, max_len, num_splits, &plan)) return 0;
+  return plan.ws_bytes;
+}
+
+int gqa_decode_num_workgroups(int B, int Hq, int Hkv, int max_len, int num_splits) {
+  DecodePlan plan;
+  if (!plan_decode(B, Hq, Hkv, 32, max_len, num_splits, &plan)) return 0;
+  return plan.n_wg;
+}
+
+int gqa_decode(int dtype, const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* cache_lens, void* o, float* lse, int B, int Hq, int Hkv, int d,
+               int max_len, float softmax_scale, int num_splits, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  DecodePlan plan;
+  if (!plan_decode(B, Hq, Hkv, d > 0 ? d : 1, max_len, num_splits, &plan))
+    return GQA_ERR_INVALID_ARG;
+  if (!q || !k_cache || !v_cache || !o) return GQA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return GQA_ERR_INVALID_ARG;
+  if ((lse && ((uintptr_t)lse & 3u)) || (cache_lens && ((uintptr_t)cache_lens & 3u)))
+    return GQA_ERR_INVALID_ARG;
+  if (!isfinite(softmax_scale)) return GQA_ERR_INVALID_ARG;
+  if (dtype != GQA_DTYPE_BF16) return GQA_ERR_UNSUPPORTED;
+  if (!supported_decode_d(d)) return GQA_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < plan.ws_bytes || !aligned16(workspace))
+    return GQA_ERR_WORKSPACE;
+
+  gqa::DecodeParams p;
+  p.q = q; p.kc = k_cache; p.vc = v_cache; p.lens = cache_lens; p.o = o; p.lse = lse;
+  p.ws_o = static_cast<float*>(workspace);
+  p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_lse_offset);
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.g = Hq / Hkv; p.d = d; p.max_len = max_len;
+  p.nqb = plan.nqb; p.n_units = plan.n_units; p.n_wg = plan.n_wg;
+  p.scale_abs = fabsf(softmax_scale);
+  p.scale_log2 = p.scale_abs * kLog2e;
+  p.negate_q = softmax_scale < 0.f ? 1 : 0;
+  // With no length array every unit has the same tile count; one share per unit then
+  // maps each workgroup onto exactly one whole unit and no merge pass is needed.
+  const bool need_combine = !(cache_lens == nullptr && plan.n_wg == plan.n_units);
+  hipError_t e = gqa::launch_decode_bf16(p, need_combine, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// gqa_kernels.h - kernel parameter blocks and launchers (internal to libgqa.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+// Prefill: one workgroup owns (sequence b, K/V head kvh, block of ROWS flattened
+// query rows). Flattened row f = i * g + head_in_group, so a block holds whole query
+// positions for every head of the group and they all share each K/V tile.
+struct PrefillParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* seqlens;
+  int B, S, Hq, Hkv, g, d;
+  float scale_log2;   // |softmax_scale| * log2(e)
+  float scale_abs;    // |softmax_scale|
+  int negate_q;       // 1 when softmax_scale < 0 (q is negated on load instead)
+  int rows_per_wg;    // flattened rows per workgroup
+  int nrb;            // row blocks per (b, kvh) unit
+  int n_wg;           // B * Hkv * nrb
+  int per_xcd;        // ceil(n_wg / 8)
+};
+
+// Decode: workgroups split the concatenated key tiles of all units
+// u = (b, kvh, query block) into equal shares (see decode_bf16.hip).
+struct DecodeParams {
+  const void* q;
+  const void* kc;
+  const void* vc;
+  const int32_t* lens;
+  void* o;
+  float* lse;
+  float* ws_o;        // [slots][32][d] normalised split outputs
+  float* ws_lse;      // [slots][32] split log-sum-exp (natural log)
+  int B, Hq, Hkv, g, d, max_len;
+  int nqb;            // query blocks per K/V head: ceil(g / 32)
+  int n_units;        // B * Hkv * nqb
+  int n_wg;           // split workgroups
+  float scale_log2;
+  float scale_abs;
+  int negate_q;
+};
+
+hipError_t launch_prefill_bf16(const PrefillParams& p, int causal, hipStream_t stream);
+hipError_t launch_prefill_f32(const PrefillParams& p, int causal, hipStream_t stream);
+hipError_t launch_decode_bf16(const DecodeParams& p, bool need_combine, hipStream_t stream);
+
+int prefill_rows_per_wg_bf16();
+int prefill_rows_per_wg_f32();
+
+}  // namespace gqa

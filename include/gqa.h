@@ -1,0 +1,150 @@
+/*
+ * gqa.h - C ABI of libgqa.so: grouped-query attention forward pass on MI355X (gfx950).
+ *
+ * Grouped-query attention splits H_q query heads into H_kv groups of
+ * g = H_q / H_kv consecutive heads; every head of a group reads the same K/V
+ * head, kv_head = q_head / g (blog.gitcode.com, "3个GQA核心优化技巧", sections
+ * "GQA的分组共享机制" and "Flash-Attention的稀疏分组优化"; azimuth.plus GQA
+ * digest, "Idea 2: grouped attention": G = H is MHA, G = 1 is MQA).
+ * The result is textbook attention, softmax(scale * Q K^T) V over the valid
+ * keys (aifullclass.xyz BERT self-attention article, LowRankSelfAttention
+ * example), computed FlashAttention-style: K/V are processed in tiles with a
+ * running max and running sum, and the score matrix never reaches HBM
+ * (webturing.pages.dev "FlashAttention Serisi", section "Ana fikir").
+ *
+ * Conventions shared by every entry point:
+ *   - All array pointers are DEVICE pointers into memory the caller owns. The
+ *     library never allocates or frees memory and keeps no pointer after a call
+ *     returns. It keeps no state between calls except a per-device cache of
+ *     the compute-unit count.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *     and the call returns right after the enqueue. No call synchronises the
+ *     host or reads device memory from the host.
+ *   - Argument errors are detected on the host before any launch; the call then
+ *     returns a non-zero gqa_status_t, launches nothing and prints nothing.
+ *   - Lengths live in device memory and cannot be checked without a
+ *     synchronisation, so the kernels clamp each length to [0, capacity].
+ *   - Every buffer base must be 16-byte aligned (128-bit loads and stores).
+ *   - Results are deterministic: the same inputs and arguments give
+ *     bitwise-identical outputs (no floating-point atomics).
+ */
+#ifndef GQA_H
+#define GQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GQA_OK = 0,
+    GQA_ERR_INVALID_ARG = 1, /* bad shape, NULL required pointer, misalignment, H_q % H_kv != 0 */
+    GQA_ERR_UNSUPPORTED = 2, /* head size or dtype this build does not provide             */
+    GQA_ERR_WORKSPACE = 3,   /* decode workspace missing or smaller than required           */
+    GQA_ERR_HIP = 4          /* the HIP runtime reported an error at launch                 */
+} gqa_status_t;
+
+typedef enum {
+    GQA_DTYPE_F32 = 0,  /* IEEE binary32 in, binary32 out, fp32 arithmetic          */
+    GQA_DTYPE_BF16 = 1  /* bfloat16 in, bfloat16 out (round to nearest even), fp32
+                           accumulation and softmax                               */
+} gqa_dtype_t;
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int gqa_version(void);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char *gqa_status_string(int status);
+
+/*
+ * gqa_prefill - self-attention over a whole sequence, bidirectional (BERT
+ * style) or causal.
+ *
+ * The pages' FlashAttention call takes separate query and K/V head counts,
+ * `causal`, `softmax_scale` (1/sqrt(d_head) by default) and a padding mask
+ * (gitcode page, "Flash-Attention的稀疏分组优化" and "阶段二：高级优化参数").
+ * Here the padding mask is given as per-sequence key lengths.
+ *
+ *   dtype          GQA_DTYPE_F32 (d in {32, 64, 128}) or GQA_DTYPE_BF16
+ *                  (d in {32, 64, 128}).
+ *   q              [B, S, Hq, d] contiguous, row-major (BSHD).
+ *   k, v           [B, S, Hkv, d] contiguous.
+ *   o              [B, S, Hq, d] output, same dtype as q. Every row is written.
+ *   lse            [B, Hq, S] fp32 natural-log log-sum-exp of the scaled scores
+ *                  of each row, or NULL. A row with no valid key gets -inf
+ *                  and O = 0.
+ *   seqlens        [B] int32 valid KEY lengths (keys j >= seqlens[b] are masked
+ *                  for every query row of sequence b; rows i >= seqlens[b] are
+ *                  still computed), or NULL for "all S keys valid". K/V rows at
+ *                  or past a length are never read, so they may hold anything.
+ *   softmax_scale  multiplies Q K^T before the softmax. Any finite value.
+ *   causal         0: every query sees every valid key. 1: query i sees keys
+ *                  j <= i (and j < seqlens[b]).
+ *   stream         hipStream_t or NULL.
+ * Returns GQA_OK, GQA_ERR_INVALID_ARG (B, S, Hq, Hkv <= 0, Hq % Hkv != 0,
+ * NULL q/k/v/o, misaligned base), GQA_ERR_UNSUPPORTED (dtype or d) or
+ * GQA_ERR_HIP.
+ */
+int gqa_prefill(int dtype, const void *q, const void *k, const void *v, void *o, float *lse,
+                const int32_t *seqlens, int B, int S, int Hq, int Hkv, int d,
+                float softmax_scale, int causal, void *stream);
+
+/*
+ * gqa_decode_workspace_bytes - device workspace gqa_decode needs for these
+ * arguments (split partials: normalised fp32 outputs and their log-sum-exp).
+ * Returns 0 for invalid arguments.
+ */
+size_t gqa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_len, int num_splits);
+
+/*
+ * gqa_decode_num_workgroups - number of split workgroups gqa_decode launches
+ * for these arguments (the auto rule when num_splits == 0). Returns 0 for
+ * invalid arguments.
+ */
+int gqa_decode_num_workgroups(int B, int Hq, int Hkv, int max_len, int num_splits);
+
+/*
+ * gqa_decode - one new query token per sequence attending to its KV cache.
+ *
+ * Each step of autoregressive generation reads the whole cached K and V of
+ * every sequence, so decode is bound by memory bandwidth, and the cache holds
+ * 2 x layers x G x d_k x n values for G K/V heads (azimuth.plus GQA digest,
+ * "the bottleneck" section and its KV-cache size formula). The work over the
+ * keys is split into pieces (the pages' `num_splits` knob, gitcode page,
+ * "阶段二：高级优化参数"); the pieces are merged with their log-sum-exp
+ * weights, which gives the same result as one pass over all keys.
+ *
+ *   dtype          GQA_DTYPE_BF16 (d in {64, 128}); fp32 is GQA_ERR_UNSUPPORTED.
+ *   q              [B, Hq, d] contiguous: the newest token of each sequence.
+ *   k_cache,
+ *   v_cache        [B, Hkv, max_len, d] contiguous.
+ *   cache_lens     [B] int32 valid lengths (keys j < cache_lens[b] are
+ *                  attended, rows at or past it are never read), or NULL for
+ *                  "all max_len rows valid". A zero length gives O = 0 and
+ *                  LSE = -inf.
+ *   o              [B, Hq, d] output, same dtype.
+ *   lse            [B, Hq] fp32 natural-log log-sum-exp, or NULL.
+ *   softmax_scale  any finite value.
+ *   num_splits     0 = automatic. n > 0: the total key work is divided into
+ *                  n x B x Hkv x ceil(g / 32) equal shares, one workgroup each;
+ *                  a sequence is split into as many pieces as shares overlap
+ *                  it, so longer caches get more splits.
+ *   workspace      device buffer of at least gqa_decode_workspace_bytes(...)
+ *                  bytes (may be NULL when that size is 0). Its contents on
+ *                  entry do not matter; calls that share a workspace must not
+ *                  overlap in time.
+ * Returns GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_WORKSPACE
+ * or GQA_ERR_HIP.
+ */
+int gqa_decode(int dtype, const void *q, const void *k_cache, const void *v_cache,
+               const int32_t *cache_lens, void *o, float *lse, int B, int Hq, int Hkv, int d,
+               int max_len, float softmax_scale, int num_splits, void *workspace,
+               size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_H */

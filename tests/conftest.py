@@ -17,3 +17,13 @@ def oracle_mod():
     import oracle
     oracle.build(force=False)
     return oracle
+
+
+@pytest.fixture(scope="session")
+def built_lib():
+    """Path of libgqa.so; compiled here only when nothing is built yet."""
+    from grouped_query_attention_02_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from grouped_query_attention_02_amd import build
+        build.build()
+    return _lib.LIB_PATH

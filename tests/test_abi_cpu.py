@@ -1,0 +1,113 @@
+"""CPU-only checks of the C ABI: the library loads, exports every declared symbol, and
+rejects invalid arguments on the host before any HIP call (no kernel is launched here)."""
+import ctypes
+import math
+
+import pytest
+
+import grouped_query_attention_02_amd as gqa
+from grouped_query_attention_02_amd import _lib
+
+F32, BF16 = _lib.GQA_DTYPE_F32, _lib.GQA_DTYPE_BF16
+INV, UNS, WS = _lib.GQA_ERR_INVALID_ARG, _lib.GQA_ERR_UNSUPPORTED, _lib.GQA_ERR_WORKSPACE
+
+# Fake, 16-byte aligned addresses: every call below fails validation before any use.
+P = 0x10000
+
+
+@pytest.fixture(scope="module")
+def lib(built_lib):
+    return _lib.load()
+
+
+def test_header_symbols_exported(lib):
+    names = _lib.header_functions()
+    assert set(names) >= {"gqa_prefill", "gqa_decode", "gqa_decode_workspace_bytes",
+                          "gqa_decode_num_workgroups", "gqa_status_string", "gqa_version"}
+    for n in names:
+        assert getattr(lib, n) is not None
+        ctypes.cast(getattr(lib, n), ctypes.c_void_p)
+
+
+def test_version_and_status_strings(lib):
+    assert gqa.version() == 10000
+    assert gqa.status_string(0) == "ok"
+    for s in (1, 2, 3, 4):
+        assert gqa.status_string(s) not in ("ok", "unknown status")
+    assert gqa.status_string(99) == "unknown status"
+
+
+def _prefill(lib, dtype=BF16, q=P, k=P, v=P, o=P, lse=None, lens=None, B=2, S=64, Hq=8, Hkv=2,
+             d=64, scale=0.125, causal=0):
+    return lib.gqa_prefill(dtype, q, k, v, o, lse, lens, B, S, Hq, Hkv, d, scale, causal, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hq=6, Hkv=4), INV),            # heads not divisible (the pages' assertion)
+    (dict(Hkv=0), INV),
+    (dict(B=0), INV),
+    (dict(S=0), INV),
+    (dict(Hq=-4), INV),
+    (dict(q=None), INV),
+    (dict(o=None), INV),
+    (dict(q=P + 2), INV),                # misaligned base
+    (dict(v=P + 8), INV),
+    (dict(lse=P + 2), INV),
+    (dict(lens=P + 1), INV),
+    (dict(causal=2), INV),
+    (dict(scale=math.inf), INV),
+    (dict(scale=math.nan), INV),
+    (dict(d=48), UNS),
+    (dict(d=256), UNS),
+    (dict(dtype=7), UNS),
+    (dict(dtype=F32, d=96), UNS),
+])
+def test_prefill_rejects(lib, kw, code):
+    assert _prefill(lib, **kw) == code
+
+
+def _decode(lib, dtype=BF16, q=P, k=P, v=P, lens=None, o=P, lse=None, B=4, Hq=32, Hkv=1, d=128,
+            max_len=1000, scale=0.1, splits=0, ws=P, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.gqa_decode_workspace_bytes(B, Hq, Hkv, d, max_len, splits)
+    return lib.gqa_decode(dtype, q, k, v, lens, o, lse, B, Hq, Hkv, d, max_len, scale, splits,
+                          ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hq=12, Hkv=5), INV),
+    (dict(B=0), INV),
+    (dict(max_len=0), INV),
+    (dict(splits=-1), INV),
+    (dict(q=None), INV),
+    (dict(k=P + 4), INV),
+    (dict(scale=-math.inf), INV),
+    (dict(dtype=F32), UNS),
+    (dict(d=32), UNS),
+    (dict(ws=None), WS),
+    (dict(ws_bytes=16), WS),
+    (dict(ws=P + 4), WS),
+])
+def test_decode_rejects(lib, kw, code):
+    assert _decode(lib, **kw) == code
+
+
+def test_decode_plan_rule(lib):
+    """Auto rule: max(units, 512) shares, capped at one share per 32-key tile; n splits: n*units."""
+    def units(B, Hq, Hkv):
+        return B * Hkv * -(-(Hq // Hkv) // 32)
+    # 32 sequences x 1 K/V head, 32 heads: 32 units -> 512 shares
+    assert gqa.decode_num_workgroups(32, 32, 1, 32768, 0) == 512
+    # 64 x 8 units (uniform 8k caches): one share per unit
+    assert gqa.decode_num_workgroups(64, 64, 8, 8192, 0) == 512
+    # tiny caches cap the shares at the tile count
+    assert gqa.decode_num_workgroups(2, 8, 2, 40, 0) == units(2, 8, 2) * 2
+    assert gqa.decode_num_workgroups(4, 8, 2, 4096, 3) == 3 * units(4, 8, 2)
+    # 64 query heads over 1 K/V head: two blocks of 32 heads per sequence
+    assert units(3, 64, 1) == 6
+    assert gqa.decode_num_workgroups(3, 64, 1, 64, 0) == 6 * 2
+    # workspace = (shares + units) slots x 32 heads x (d + 1) floats
+    W, U = 512, 32
+    assert gqa.decode_workspace_bytes(32, 32, 1, 128, 32768, 0) == (W + U) * 32 * 129 * 4
+    assert gqa.decode_workspace_bytes(32, 32, 1, 128, 0, 0) == 0
+    assert gqa.decode_workspace_bytes(32, 30, 4, 128, 100, 0) == 0
