@@ -1,0 +1,278 @@
+"""Benchmark of the GQA forward hot path on one MI355X.
+
+One step = one pass of the whole hot path on resident, seeded synthetic inputs:
+  1. gqa_prefill on the BERT-base-shaped bidirectional workload (batch 32, seq 1024,
+     12 query heads over 3 K/V heads, d 64, bf16, key lengths uniform in [512, 1024]);
+  2. gqa_decode on the multi-query ragged workload (32 sequences, 32 query heads over
+     1 K/V head, d 128, bf16, cache lengths uniform in [1024, 32768], split-KV + combine).
+`value` is the prefill rate in TFLOP/s (algorithmic FLOPs / measured launch time) and
+the line's `decode` object carries the decode KV-cache GB/s; both are timed with HIP
+events on the stream the kernels run on, inside the K timed steps. After the timed
+steps, the causal Llama-style prefill and the uniform 8k decode are timed the same way
+and reported under `also` (not part of `value`).
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GQA prefill TFLOP/s (% MFMA peak) + decode KV-cache GB/s (% HBM) on 1 MI355X"
+
+
+def _events(n):
+    import torch
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(n)]
+
+
+def _ms(evs):
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def _prefill_case(w, dev):
+    import torch
+    import workloads as W
+    from grouped_query_attention_02_amd import perfmodel
+    x = W.make_prefill(w, device="cpu")
+    q, k, v = x["q"].to(dev), x["k"].to(dev), x["v"].to(dev)
+    lens = None if x["seqlens"] is None else x["seqlens"].to(dev)
+    lens_host = None if x["seqlens"] is None else x["seqlens"].tolist()
+    flops = perfmodel.prefill_flops(w.B, w.S, w.Hq, w.d, w.causal, lens_host)
+    out = torch.empty_like(q)
+    return dict(w=w, q=q, k=k, v=v, lens=lens, lens_host=lens_host, flops=flops, out=out,
+                host=x)
+
+
+def _decode_case(w, dev):
+    import torch
+    import workloads as W
+    import grouped_query_attention_02_amd as gqa
+    from grouped_query_attention_02_amd import perfmodel
+    x = W.make_decode(w, device="cpu")
+    q, kc, vc, lens = (x["q"].to(dev), x["k_cache"].to(dev), x["v_cache"].to(dev),
+                       x["lens"].to(dev))
+    lens_host = x["lens"].tolist()
+    nbytes = perfmodel.decode_bytes(w.B, w.Hq, w.Hkv, w.d, lens_host, w.max_len, 2)
+    ws = torch.empty(max(16, gqa.decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.d, w.max_len, 0)),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    del x
+    return dict(w=w, q=q, kc=kc, vc=vc, lens=lens, lens_host=lens_host, bytes=nbytes, ws=ws,
+                out=out)
+
+
+def _run_prefill(c):
+    import grouped_query_attention_02_amd as gqa
+    w = c["w"]
+    gqa.prefill(c["q"], c["k"], c["v"], causal=w.causal, softmax_scale=w.softmax_scale,
+                seqlens=c["lens"], out=c["out"])
+
+
+def _run_decode(c):
+    import grouped_query_attention_02_amd as gqa
+    w = c["w"]
+    gqa.decode(c["q"], c["kc"], c["vc"], c["lens"], softmax_scale=w.softmax_scale,
+               workspace=c["ws"], out=c["out"])
+
+
+def _time_loop(fn, c, reps, warm):
+    import torch
+    for _ in range(warm):
+        fn(c)
+    evs = _events(reps)
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record()
+        fn(c)
+        b.record()
+    torch.cuda.synchronize()
+    return _ms(evs)
+
+
+def _cpu_baseline(pc, target_s: float):
+    """The fp64 oracle, as it stands, on a random row sample of the prefill workload."""
+    import numpy as np
+    import oracle
+    w = pc["w"]
+    x = pc["host"]
+    lens = x["seqlens"].numpy() if x["seqlens"] is not None else np.full(w.B, w.S)
+    rng = np.random.default_rng(0)
+
+    def sample(n):
+        return np.stack([rng.integers(w.B, size=n), rng.integers(w.Hq, size=n),
+                         rng.integers(w.S, size=n)], 1).astype(np.int64)
+
+    def flops(rows):
+        return sum(4 * w.d * (min(int(i) + 1, int(lens[b])) if w.causal else int(lens[b]))
+                   for b, h, i in rows)
+
+    pilot = sample(2000)
+    t = time.perf_counter()
+    oracle.prefill_rows(x["q"], x["k"], x["v"], pilot, scale=w.softmax_scale, causal=w.causal,
+                        seqlens=x["seqlens"])
+    rate = flops(pilot) / max(time.perf_counter() - t, 1e-6)
+    total_rows = w.B * w.S * w.Hq
+    n = int(min(total_rows, max(2000, rate * target_s / (4 * w.d * float(np.mean(lens))))))
+    rows = sample(n)
+    t = time.perf_counter()
+    oracle.prefill_rows(x["q"], x["k"], x["v"], rows, scale=w.softmax_scale, causal=w.causal,
+                        seqlens=x["seqlens"])
+    dt = time.perf_counter() - t
+    return {"value": flops(rows) / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"{n} random (b, head, query) rows of {w.name} ({n / total_rows:.1%} of "
+                      f"its {total_rows} rows), fp64, {dt:.1f} s wall"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the extra workloads")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+    import workloads as W
+    import grouped_query_attention_02_amd as gqa
+    from grouped_query_attention_02_amd import perfmodel
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    gqa.load()
+    dev = torch.device("cuda:0")
+    print(f"[bench] device {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
+
+    pc = _prefill_case(W.WORKLOADS["bert_base_prefill"], dev)
+    dc = _decode_case(W.WORKLOADS["mqa_ragged_decode"], dev)
+    print(f"[bench] inputs ready: prefill {pc['flops'] / 1e9:.2f} GFLOP, decode "
+          f"{dc['bytes'] / 1e6:.2f} MB (sum of cache lengths {sum(dc['lens_host'])})",
+          file=sys.stderr, flush=True)
+
+    # warmup steps (untimed)
+    for _ in range(args.warmup):
+        _run_prefill(pc)
+        _run_decode(dc)
+    torch.cuda.synchronize()
+
+    pev, dev_ev = _events(args.steps), _events(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        pev[i][0].record()
+        _run_prefill(pc)
+        pev[i][1].record()
+        dev_ev[i][0].record()
+        _run_decode(dc)
+        dev_ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    p_ms, d_ms = _ms(pev), _ms(dev_ev)
+    print(f"[bench] timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
+
+    p_avg = statistics.mean(p_ms)
+    d_avg = statistics.mean(d_ms)
+    p_tflops = pc["flops"] / (p_avg * 1e-3) / 1e12
+    d_gbps = dc["bytes"] / (d_avg * 1e-3) / 1e9
+
+    also = {}
+    if not args.no_extra:
+        lc = _prefill_case(W.WORKLOADS["llama_causal_prefill"], dev)
+        ms = _time_loop(_run_prefill, lc, max(10, args.steps // 2), 3)
+        also["llama_causal_prefill"] = {
+            "tflops": lc["flops"] / (statistics.mean(ms) * 1e-3) / 1e12,
+            "frac_mfma_peak": lc["flops"] / (statistics.mean(ms) * 1e-3) / 1e12
+            / perfmodel.PEAK_BF16_TFLOPS,
+            "ms_mean": statistics.mean(ms), "ms_min": min(ms), "flops": lc["flops"]}
+        del lc
+        torch.cuda.empty_cache()
+        gc = _decode_case(W.WORKLOADS["gqa_decode_8k"], dev)
+        ms = _time_loop(_run_decode, gc, max(10, args.steps // 2), 3)
+        also["gqa_decode_8k"] = {
+            "gbps": gc["bytes"] / (statistics.mean(ms) * 1e-3) / 1e9,
+            "frac_hbm_peak": gc["bytes"] / (statistics.mean(ms) * 1e-3) / 1e9
+            / perfmodel.PEAK_HBM_GBPS,
+            "ms_mean": statistics.mean(ms), "ms_min": min(ms), "bytes": gc["bytes"]}
+        del gc
+        torch.cuda.empty_cache()
+        tc = _prefill_case(W.WORKLOADS["tiny_f32_prefill"], dev)
+        ms = _time_loop(_run_prefill, tc, 20, 3)
+        also["tiny_f32_prefill"] = {"us_mean": statistics.mean(ms) * 1e3,
+                                    "tflops": tc["flops"] / (statistics.mean(ms) * 1e-3) / 1e12}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        cpu = _cpu_baseline(pc, args.cpu_seconds)
+
+    wp = pc["w"]
+    wd = dc["w"]
+    line = {
+        "metric": METRIC,
+        "value": round(p_tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round((p_avg + d_avg), 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) bf16 inputs, uniform random lengths",
+        "config": {
+            "workload": "bert_base_prefill + mqa_ragged_decode",
+            "prefill": {"name": wp.name, "B": wp.B, "S": wp.S, "Hq": wp.Hq, "Hkv": wp.Hkv,
+                        "d": wp.d, "causal": wp.causal, "key_lengths": list(wp.lens),
+                        "seed": wp.seed, "sum_key_len": sum(pc["lens_host"])},
+            "decode": {"name": wd.name, "B": wd.B, "Hq": wd.Hq, "Hkv": wd.Hkv, "d": wd.d,
+                       "max_len": wd.max_len, "cache_lengths": list(wd.lens), "seed": wd.seed,
+                       "sum_cache_len": sum(dc["lens_host"]),
+                       "split_workgroups": gqa.decode_num_workgroups(wd.B, wd.Hq, wd.Hkv,
+                                                                     wd.max_len, 0)},
+        },
+        "roofline": {
+            "bound": "mfma", "achieved": round(p_tflops, 3),
+            "peak": perfmodel.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(p_tflops / perfmodel.PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "kernel": "prefill_bf16_kernel<64, non-causal>",
+            "launch_us_mean": round(p_avg * 1e3, 2), "flops_per_launch": pc["flops"],
+        },
+        "decode": {
+            "gbps": round(d_gbps, 2), "frac_hbm_peak": round(d_gbps / perfmodel.PEAK_HBM_GBPS, 4),
+            "peak_gbps": perfmodel.PEAK_HBM_GBPS, "call_us_mean": round(d_avg * 1e3, 2),
+            "call_us_min": round(min(d_ms) * 1e3, 2), "bytes_per_call": dc["bytes"],
+            "kernels": "decode_split_kernel<128> + decode_combine_kernel<128>",
+        },
+        "cpu_baseline": cpu,
+        "also": also,
+        "context": "pages: ~980 tokens/s for a whole BERT-base model on A100 at seq 1024, "
+                   "batch 32, precision unstated; not comparable to an attention-kernel rate",
+        "host": platform.node(),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

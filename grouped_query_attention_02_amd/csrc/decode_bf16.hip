@@ -349,9 +349,13 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_split_kernel(DecodeParam
   }
 }
 
-// Merge the split partials of one unit (b, kvh, query block).
+// Merge the split partials of one unit (b, kvh, query block): workgroup (u, head block),
+// one thread per (head, 4 output columns). Partials are visited in workgroup order with
+// a running max, so the merge order is fixed and the result deterministic.
 template <int D>
 __global__ __launch_bounds__(DC_THREADS) void decode_combine_kernel(DecodeParams p) {
+  constexpr int TPH = D / 4;              // threads per head
+  constexpr int HPB = DC_THREADS / TPH;   // heads per workgroup
   __shared__ long long scratch[DC_WAVES + 2];
   const int u = blockIdx.x;
   const int qb = u % p.nqb;
@@ -365,11 +369,15 @@ __global__ __launch_bounds__(DC_THREADS) void decode_combine_kernel(DecodeParams
   const int Tb = tiles_of(clamp_len(p.lens, b, cap));
   const int hbase = kvh * p.g + qb * 32;
   const int nh = min(32, p.g - qb * 32);
-  uint16_t* obase = static_cast<uint16_t*>(p.o) + ((size_t)b * p.Hq + hbase) * D;
+  const int n = blockIdx.y * HPB + threadIdx.x / TPH;
+  const int d0 = (threadIdx.x % TPH) * 4;
+  if (n >= nh) return;
+  uint16_t* orow = static_cast<uint16_t*>(p.o) + ((size_t)b * p.Hq + hbase + n) * D + d0;
+  float* lse_out = p.lse ? p.lse + (size_t)b * p.Hq + hbase + n : nullptr;
 
   if (Tb == 0) {  // empty cache: O = 0, LSE = -inf
-    for (int idx = threadIdx.x; idx < nh * D; idx += DC_THREADS) obase[idx] = 0;
-    if (p.lse && threadIdx.x < nh) p.lse[(size_t)b * p.Hq + hbase + threadIdx.x] = -INFINITY;
+    *reinterpret_cast<u32x2*>(orow) = u32x2{0u, 0u};
+    if (lse_out && d0 == 0) *lse_out = -INFINITY;
     return;
   }
   const long long W = T < p.n_wg ? T : p.n_wg;  // the split kernel's effective share count
@@ -379,29 +387,40 @@ __global__ __launch_bounds__(DC_THREADS) void decode_combine_kernel(DecodeParams
   const int wb = (int)(((ulast + 1) * W - 1) / T);
   if (wa == wb) return;  // one workgroup covered the unit and wrote the output
 
-  for (int idx = threadIdx.x; idx < nh * (D / 4); idx += DC_THREADS) {
-    const int n = idx / (D / 4);
-    const int d0 = (idx - n * (D / 4)) * 4;
-    float M = -INFINITY;
-    for (int wv = wa; wv <= wb; ++wv) M = fmaxf(M, p.ws_lse[((size_t)wv + u) * 32 + n]);
-    float den = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int wv = wa; wv <= wb; ++wv) {
-      const size_t slot = (size_t)wv + u;
-      const float lw = p.ws_lse[slot * 32 + n];
-      const float e = (lw == -INFINITY) ? 0.f : fast_exp2((lw - M) * kLog2e);
-      den += e;
-      const u32x4 ov = ldg16(p.ws_o + (slot * 32 + n) * D + d0);
+  float m = -INFINITY, den = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = wa; s0 <= wb; s0 += 8) {
+    float lw[8];
+    u32x4 ov[8];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) acc[k] += e * __uint_as_float(ov[k]);
+    for (int k = 0; k < 8; ++k) {
+      const int s = s0 + k;
+      if (s <= wb) {
+        const size_t slot = (size_t)s + u;
+        lw[k] = p.ws_lse[slot * 32 + n];
+        ov[k] = ldg16(p.ws_o + (slot * 32 + n) * D + d0);
+      } else {
+        lw[k] = -INFINITY;
+        ov[k] = zero_u32x4();
+      }
     }
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-    u32x2 o2;
-    o2[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-    o2[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-    *reinterpret_cast<u32x2*>(obase + (size_t)n * D + d0) = o2;
-    if (p.lse && d0 == 0)
-      p.lse[(size_t)b * p.Hq + hbase + n] = den > 0.f ? M + logf(den) : -INFINITY;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (lw[k] == -INFINITY) continue;
+      const float m_new = fmaxf(m, lw[k]);
+      const float sc = (m == -INFINITY) ? 0.f : fast_exp2((m - m_new) * kLog2e);
+      const float e = fast_exp2((lw[k] - m_new) * kLog2e);
+      den = den * sc + e;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[c] = acc[c] * sc + e * __uint_as_float(ov[k][c]);
+      m = m_new;
+    }
   }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  u32x2 o2;
+  o2[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  o2[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  *reinterpret_cast<u32x2*>(orow) = o2;
+  if (lse_out && d0 == 0) *lse_out = den > 0.f ? m + logf(den) : -INFINITY;
 }
 
 template <int D>
@@ -416,7 +435,10 @@ hipError_t launch_d(const DecodeParams& p, bool need_combine, hipStream_t stream
   hipLaunchKernelGGL(kern, dim3(p.n_wg), dim3(DC_THREADS), lds, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess || !need_combine) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(p.n_units), dim3(DC_THREADS), 0, stream, p);
+  constexpr int HPB = DC_THREADS / (D / 4);
+  const int heads = p.g < 32 ? p.g : 32;
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(p.n_units, (heads + HPB - 1) / HPB),
+                     dim3(DC_THREADS), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -16,6 +16,7 @@ constexpr int kVersion = 10000;  // 1.0.0
 constexpr int kDecodeTile = 32;  // keys per decode tile
 constexpr int kDecodeAutoShares = 512;  // auto split: at least 2 workgroups per CU of a 256-CU GPU
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kMinScaleLog2 = 1e-30f;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -97,7 +98,9 @@ int gqa_prefill(int dtype, const void* q, const void* k, const void* v, void* o,
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse; p.seqlens = seqlens;
   p.B = B; p.S = S; p.Hq = Hq; p.Hkv = Hkv; p.g = g; p.d = d;
   p.scale_abs = fabsf(softmax_scale);
-  p.scale_log2 = p.scale_abs * kLog2e;
+  // A zero scale (uniform weights) still gets a positive exponent factor, tiny enough
+  // that every valid weight rounds to exp2(0) = 1 while masked scores (-inf) give 0.
+  p.scale_log2 = fmaxf(p.scale_abs * kLog2e, kMinScaleLog2);
   p.negate_q = softmax_scale < 0.f ? 1 : 0;
   p.rows_per_wg = dtype == GQA_DTYPE_BF16 ? gqa::prefill_rows_per_wg_bf16()
                                           : gqa::prefill_rows_per_wg_f32();
@@ -152,7 +155,9 @@ int gqa_decode(int dtype, const void* q, const void* k_cache, const void* v_cach
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.g = Hq / Hkv; p.d = d; p.max_len = max_len;
   p.nqb = plan.nqb; p.n_units = plan.n_units; p.n_wg = plan.n_wg;
   p.scale_abs = fabsf(softmax_scale);
-  p.scale_log2 = p.scale_abs * kLog2e;
+  // A zero scale (uniform weights) still gets a positive exponent factor, tiny enough
+  // that every valid weight rounds to exp2(0) = 1 while masked scores (-inf) give 0.
+  p.scale_log2 = fmaxf(p.scale_abs * kLog2e, kMinScaleLog2);
   p.negate_q = softmax_scale < 0.f ? 1 : 0;
   // With no length array every unit has the same tile count; one share per unit then
   // maps each workgroup onto exactly one whole unit and no merge pass is needed.

@@ -8,21 +8,29 @@
 // reused by all g heads of the group (same section: K/V reuse in on-chip memory,
 // access granularity raised from a head to a block).
 //
-// Per K/V tile of 64 keys, each of the 8 waves (32 rows each):
-//   S^T = K Q^T          2 x (d/16) MFMA 32x32x16 (A = K rows from LDS, B = Q in VGPRs)
-//   mask, online softmax running max / running sum (webturing.pages.dev
-//   "FlashAttention Serisi", section "Ana fikir": the softmax is built as a
+// Per K/V tile of 64 keys, each of the 8 waves (32 rows each) computes
+//   S^T = K Q^T          (A = K rows from LDS, B = Q held in VGPRs)
+//   mask, online softmax with a running max and running sum (webturing.pages.dev
+//   "FlashAttention Serisi", section "Ana fikir": the softmax is accumulated as a
 //   running sum so the score matrix never leaves the chip)
-//   O^T += V^T P^T       (d/32) x 4 MFMA (A = V^T from LDS, B = P straight from the
-//                        score accumulators, no LDS round trip)
-// The result equals textbook softmax(scale Q K^T) V over the valid keys (aifullclass.xyz
-// BERT self-attention article, LowRankSelfAttention example; the FlashAttention page's
-// FAQ: the computed result is mathematically the same).
+//   O^T += V^T P^T       (A = V^T read from row-major LDS with the transposing
+//                        ds_read_b64_tr_b16, B = P taken straight from the score
+//                        accumulators)
+// on v_mfma_f32_32x32x16_bf16. The loop is software-pipelined: iteration t issues the
+// PV product of tile t-1 and the QK^T product of tile t+1 on the matrix cores while the
+// vector ALUs run the softmax of tile t. The running max used as the exponent offset is
+// refreshed only when a row's max grows by more than 2^8 (in exp2 units), so the O
+// rescale is rare; the result is the same normalised softmax because every term of a
+// row always shares one offset. The result equals textbook softmax(scale Q K^T) V over
+// the valid keys (aifullclass.xyz BERT self-attention article, LowRankSelfAttention
+// example; FlashAttention page FAQ: the computed result is mathematically the same).
 //
 // Masks: key j is visible to query i iff j < L_b and (not causal or j <= i). K/V rows
 // at or past L_b are never read (zero-filled in LDS), so padding may hold anything.
 #include "gqa_device.h"
 #include "gqa_kernels.h"
+
+#include <type_traits>
 
 namespace gqa {
 namespace {
@@ -31,25 +39,32 @@ constexpr int PF_WAVES = 8;
 constexpr int PF_THREADS = 64 * PF_WAVES;
 constexpr int PF_ROWS = 32 * PF_WAVES;  // flattened query rows per workgroup
 constexpr int PF_BN = 64;               // keys per K/V tile
+constexpr float kTau = 8.0f;            // exp2 headroom before the running max is refreshed
+
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 template <int D>
 struct PfLayout {
-  static constexpr int KSTR = D + 8;       // bf16 per K row in LDS (pad: conflict-free b128 reads)
-  static constexpr int VSTR = PF_BN + 4;   // bf16 per V^T row in LDS (pad: conflict-free b64 reads)
-  static constexpr int K_ELEMS = PF_BN * KSTR;
-  static constexpr int V_ELEMS = D * VSTR;
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;
-  static constexpr int CPR = D / 8;                               // 16-byte chunks per row
-  static constexpr int KCH = PF_BN * CPR;                         // K chunks per tile
-  static constexpr int KPT = (KCH + PF_THREADS - 1) / PF_THREADS;
-  static constexpr int VBL = (PF_BN / 2) * CPR;                   // (2 keys x 8 d) V blocks
-  static constexpr int VPT = (VBL + PF_THREADS - 1) / PF_THREADS;
+  // K rows: stride = 4 dwords mod 64 banks -> conflict-free 16-byte fragment reads.
+  static constexpr int KSTR = D + 8;
+  // V rows: stride = 16 (or 48) dwords mod 64 banks -> conflict-free transposing reads.
+  static constexpr int VSTR = D == 32 ? 32 : D + 32;
+  static constexpr int K_EL = PF_BN * KSTR;
+  static constexpr int V_EL = PF_BN * VSTR;
+  static constexpr int LDS_BYTES = 2 * (K_EL + V_EL) * 2;
+  static constexpr int CPR = D / 8;                      // 16-byte chunks per row
+  static constexpr int CH = PF_BN * CPR;                 // chunks per K (or V) tile
+  static constexpr int CPT = (CH + PF_THREADS - 1) / PF_THREADS;
 };
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(PF_THREADS, 1) void prefill_bf16_kernel(PrefillParams p) {
   using Lay = PfLayout<D>;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  // LDS: K buffers 0 and 1, then V buffers 0 and 1.
+  auto kbuf = [&](int i) { return smem + (i & 1) * Lay::K_EL; };
+  auto vbuf = [&](int i) { return smem + 2 * Lay::K_EL + (i & 1) * Lay::V_EL; };
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -95,6 +110,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_bf16_kernel(PrefillPara
   }
   const int lim = CAUSAL ? min(Lb, qi + 1) : Lb;  // keys j < lim are visible to this row
   const int ntiles = (kv_end + PF_BN - 1) / PF_BN;
+  const int wave_nt = (wave_kv_end + PF_BN - 1) / PF_BN;
 
   // Q^T as the B operand: lane holds query row f, d = ks*16 + hh*8 .. +7.
   bf16x8 qf[D / 16];
@@ -114,149 +130,187 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_bf16_kernel(PrefillPara
   const uint16_t* kbase = static_cast<const uint16_t*>(p.k) + ((size_t)b * S * Hkv + kvh) * D;
   const uint16_t* vbase = static_cast<const uint16_t*>(p.v) + ((size_t)b * S * Hkv + kvh) * D;
 
-  u32x4 kreg[Lay::KPT], va[Lay::VPT], vb[Lay::VPT];
-
-  auto gload = [&](int t0) {
+  // ---- global -> register -> LDS staging of one K or V tile (rows >= L_b are zeros)
+  u32x4 kst[Lay::CPT], vst[Lay::CPT];
+  auto gload = [&](u32x4 (&st)[Lay::CPT], const uint16_t* base, int tile) {
+    const int t0 = tile * PF_BN;
 #pragma unroll
-    for (int r = 0; r < Lay::KPT; ++r) {
-      const int c = tid + r * PF_THREADS;
-      if (Lay::KCH % PF_THREADS == 0 || c < Lay::KCH) {
-        const int key = c / Lay::CPR, col = c - key * Lay::CPR;
+    for (int r = 0; r < Lay::CPT; ++r) {
+      const int id = tid + r * PF_THREADS;
+      if (Lay::CH % PF_THREADS == 0 || id < Lay::CH) {
+        const int key = id / Lay::CPR, col = id - key * Lay::CPR;
         const int j = t0 + key;
-        kreg[r] = j < Lb ? ldg16(kbase + (size_t)j * rstride + col * 8) : zero_u32x4();
+        st[r] = j < Lb ? ldg16(base + (size_t)j * rstride + col * 8) : zero_u32x4();
       }
     }
+  };
+  auto lstore = [&](const u32x4 (&st)[Lay::CPT], uint16_t* dst, int stride) {
 #pragma unroll
-    for (int r = 0; r < Lay::VPT; ++r) {
-      const int c = tid + r * PF_THREADS;
-      if (Lay::VBL % PF_THREADS == 0 || c < Lay::VBL) {
-        const int pr = c / Lay::CPR, col = c - pr * Lay::CPR;
-        const int j = t0 + 2 * pr;
-        va[r] = j < Lb ? ldg16(vbase + (size_t)j * rstride + col * 8) : zero_u32x4();
-        vb[r] = j + 1 < Lb ? ldg16(vbase + (size_t)(j + 1) * rstride + col * 8) : zero_u32x4();
+    for (int r = 0; r < Lay::CPT; ++r) {
+      const int id = tid + r * PF_THREADS;
+      if (Lay::CH % PF_THREADS == 0 || id < Lay::CH) {
+        const int key = id / Lay::CPR, col = id - key * Lay::CPR;
+        *reinterpret_cast<u32x4*>(dst + key * stride + col * 8) = st[r];
       }
     }
   };
 
-  // K rows as loaded; V transposed in registers so each LDS row holds one d for all keys.
-  auto lstore = [&](int stage) {
-    uint16_t* ks_ = smem + stage * Lay::STAGE;
-    uint16_t* vs_ = ks_ + Lay::K_ELEMS;
-#pragma unroll
-    for (int r = 0; r < Lay::KPT; ++r) {
-      const int c = tid + r * PF_THREADS;
-      if (Lay::KCH % PF_THREADS == 0 || c < Lay::KCH) {
-        const int key = c / Lay::CPR, col = c - key * Lay::CPR;
-        *reinterpret_cast<u32x4*>(ks_ + key * Lay::KSTR + col * 8) = kreg[r];
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < Lay::VPT; ++r) {
-      const int c = tid + r * PF_THREADS;
-      if (Lay::VBL % PF_THREADS == 0 || c < Lay::VBL) {
-        const int pr = c / Lay::CPR, col = c - pr * Lay::CPR;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t a = va[r][e], bb = vb[r][e];
-          const uint32_t lo = (a & 0xffffu) | (bb << 16);
-          const uint32_t hi = (a >> 16) | (bb & 0xffff0000u);
-          *reinterpret_cast<uint32_t*>(vs_ + (col * 8 + 2 * e) * Lay::VSTR + 2 * pr) = lo;
-          *reinterpret_cast<uint32_t*>(vs_ + (col * 8 + 2 * e + 1) * Lay::VSTR + 2 * pr) = hi;
-        }
-      }
-    }
-  };
-
+  // ---- matrix-core phases
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) oacc[i] = zero16();
+
+  // S^T = K Q^T for two 32-key blocks: lane holds query l32, keys 8(r/4)+4hh+(r%4).
+  auto qk = [&](f32x16 (&s)[2], const uint16_t* kb_) {
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const u32x4 a =
+            *reinterpret_cast<const u32x4*>(kb_ + (kb * 32 + l32) * Lay::KSTR + ks * 16 + hh * 8);
+        s[kb] = mfma_bf16_32x32x16(as_bf16x8(a), qf[ks], ks == 0 ? zero16() : s[kb]);
+      }
+    }
+  };
+  // O^T += V^T P^T, 16 keys per MFMA; B slot i <-> key 16ks + 8(i/4) + 4hh + (i%4).
+  // The transposing read hands lane (group G = lane/16, i = lane%16) keys
+  // 16ks + 4(G/2) + {0..3} (and +8) of output column d = db*32 + (lane % 32).
+  const int tr_row = 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  auto pv = [&](const bf16x8 (&pp)[4], const uint16_t* vb_) {
+#pragma unroll
+    for (int ks = 0; ks < PF_BN / 16; ++ks) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const uint16_t* a0 = vb_ + (ks * 16 + tr_row) * Lay::VSTR + db * 32 + tr_col;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0 + 8 * Lay::VSTR));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        const u32x4 a = {l2[0], l2[1], h2[0], h2[1]};
+        oacc[db] = mfma_bf16_32x32x16(as_bf16x8(a), pp[ks], oacc[db]);
+      }
+    }
+  };
+
+  // ---- online softmax state (one query row per lane; lanes l and l^32 share a row)
   float m_run = -INFINITY, l_run = 0.f;
   const float c = p.scale_log2;
 
+  auto mask = [&](f32x16 (&s)[2], int t0) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = t0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (j >= lim) s[kb][r] = -INFINITY;
+      }
+  };
+  // Returns this lane's rescale factor for O; P goes to pp as bf16.
+  auto softmax = [&](f32x16 (&s)[2], bf16x8 (&pp)[4]) -> float {
+    float mx = m_run;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = fmaxf(mx, xor32(mx));  // the other 32 keys of this row sit in lane l ^ 32
+    const bool fresh = m_run == -INFINITY;
+    const bool refresh = fresh ? (mx != -INFINITY) : ((mx - m_run) * c > kTau);
+    const float m_new = refresh ? mx : m_run;
+    const float alpha = refresh ? (fresh ? 0.f : fast_exp2((m_run - m_new) * c)) : 1.f;
+    m_run = m_new;
+    const float msc = (m_new == -INFINITY ? 0.f : m_new) * c;
+    float lsum = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int kb = ks >> 1, r0 = 8 * (ks & 1);
+      float e[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        e[i] = fast_exp2(fmaf(s[kb][r0 + i], c, -msc));  // masked: exp2(-inf) = 0 as c > 0
+      }
+      u32x4 u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u[i] = pack_bf16x2(e[2 * i], e[2 * i + 1]);
+        lsum += e[2 * i] + e[2 * i + 1];
+      }
+      pp[ks] = as_bf16x8(u);
+    }
+    l_run = l_run * alpha + lsum;
+    return alpha;
+  };
+  auto rescale = [&](float alpha) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+  };
+
+  // ---- pipeline: iteration t runs PV(t-1), QK(t+1) and softmax(t); LDS holds
+  // K(t+1), V(t-1) while K(t+2), V(t) are fetched from HBM. Every wave runs every tile
+  // of the workgroup (tiles past a causal wave's rows are fully masked and add nothing);
+  // the QK of the last iteration reads a stale K buffer and its result is discarded.
+  // The loop is unrolled by two with the register roles swapped, so no accumulator is
+  // ever copied.
+  f32x16 s_a[2], s_b[2];
+  bf16x8 pp_a[4], pp_b[4];
   if (ntiles > 0) {
-    gload(0);
-    lstore(0);
+    gload(kst, kbase, 0);
+    if (ntiles > 1) gload(vst, kbase, 1);  // K(1) staged through the V registers
+    lstore(kst, kbuf(0), Lay::KSTR);
+    if (ntiles > 1) lstore(vst, kbuf(1), Lay::KSTR);
   }
   __syncthreads();
+  if (ntiles > 0) qk(s_a, kbuf(0));
+  __syncthreads();  // every wave has read K(0) before K(2) replaces it
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int t0 = t * PF_BN;
-    const bool has_next = t + 1 < ntiles;
-    if (has_next) gload(t0 + PF_BN);
-    const uint16_t* ks_ = smem + (t & 1) * Lay::STAGE;
-    const uint16_t* vs_ = ks_ + Lay::K_ELEMS;
-
-    if (t0 < wave_kv_end) {
-      // S^T = K Q^T for two 32-key blocks: lane holds query l32, keys 8(r/4)+4hh+(r%4).
-      f32x16 s[2];
+  auto step = [&](auto do_pv, int t, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
+                  bf16x8 (&pp_prev)[4], bf16x8 (&pp_cur)[4]) {
+    __builtin_amdgcn_sched_barrier(0);
+    const bool more_k = t + 2 < ntiles;
+    if (more_k) gload(kst, kbase, t + 2);
+    gload(vst, vbase, t);
+    if (t * PF_BN + PF_BN > wave_mask_from) mask(s_cur, t * PF_BN);
+    __builtin_amdgcn_sched_barrier(0);
+    // One scheduling region: matrix-core products of tiles t-1 and t+1 interleaved with
+    // the vector-ALU softmax of tile t (each MFMA is followed by a slice of the VALU work,
+    // with the LDS fragment reads kept one MFMA ahead).
+    constexpr bool kPV = decltype(do_pv)::value;
+    if constexpr (kPV) pv(pp_prev, vbuf((t - 1) & 1));
+    qk(s_nxt, kbuf((t + 1) & 1));
+    const float alpha = softmax(s_cur, pp_cur);
+    constexpr int kMfma = (kPV ? 4 * (D / 32) : 0) + 2 * (D / 16);
+    constexpr int kValuPer = (kMfma >= 32 ? 4 : (kMfma >= 16 ? 7 : 14));
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = zero16();
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const u32x4 a =
-              *reinterpret_cast<const u32x4*>(ks_ + (kb * 32 + l32) * Lay::KSTR + ks * 16 + hh * 8);
-          s[kb] = mfma_bf16_32x32x16(as_bf16x8(a), qf[ks], s[kb]);
-        }
-      }
-
-      const bool need_mask = t0 + PF_BN > wave_mask_from;
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = t0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (j >= lim) s[kb][r] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = fmaxf(mx, xor32(mx));  // the other 32 keys of this query sit in lane l ^ 32
-      const float m_new = fmaxf(m_run, mx);
-      if (wave_any(m_new > m_run)) {
-        const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_new) * c);
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-        m_run = m_new;
-      }
-      const float msc = (m_run == -INFINITY ? 0.f : m_run) * c;
-      float lsum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float pv = fast_exp2(fmaf(s[kb][r], c, -msc));
-          if (need_mask) pv = (s[kb][r] == -INFINITY) ? 0.f : pv;
-          s[kb][r] = pv;
-          lsum += pv;
-        }
-      l_run += lsum;
-
-      // O^T += V^T P^T, 16 keys per MFMA: B slot i <-> key 16ks + 8(i/4) + 4hh + (i%4).
-#pragma unroll
-      for (int ks = 0; ks < PF_BN / 16; ++ks) {
-        const int kb = ks >> 1, r0 = 8 * (ks & 1);
-        const bf16x8 pb = pack_bf16x8(s[kb][r0 + 0], s[kb][r0 + 1], s[kb][r0 + 2], s[kb][r0 + 3],
-                                      s[kb][r0 + 4], s[kb][r0 + 5], s[kb][r0 + 6], s[kb][r0 + 7]);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const uint16_t* vp = vs_ + (db * 32 + l32) * Lay::VSTR + ks * 16 + 4 * hh;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 8);
-          const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-          oacc[db] = mfma_bf16_32x32x16(as_bf16x8(a), pb, oacc[db]);
-        }
-      }
+    for (int i = 0; i < kMfma; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kValuPer, 0);
     }
-    if (has_next) lstore((t + 1) & 1);
+    // Pin P(t) here: without a use inside the region the compiler sinks the exponentials
+    // into the next step, next to their consumer, and nothing overlaps the MFMAs.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" ::"v"(pp_cur[i]));
+    __builtin_amdgcn_sched_barrier(0);
+    if (wave_any(alpha != 1.f)) rescale(alpha);  // after PV(t-1), before PV(t)
+    if (more_k) lstore(kst, kbuf(t & 1), Lay::KSTR);
+    lstore(vst, vbuf(t & 1), Lay::VSTR);
     __syncthreads();
+  };
+  using no_pv = std::integral_constant<bool, false>;
+  using with_pv = std::integral_constant<bool, true>;
+  int t = 1;
+  if (ntiles > 0) {
+    step(no_pv{}, 0, s_a, s_b, pp_b, pp_a);
+    for (; t + 1 < ntiles; t += 2) {
+      step(with_pv{}, t, s_b, s_a, pp_a, pp_b);
+      step(with_pv{}, t + 1, s_a, s_b, pp_b, pp_a);
+    }
+    if (t < ntiles) step(with_pv{}, t, s_b, s_a, pp_a, pp_b);
+    // PV of the last tile: its P sits in pp_a when ntiles is odd, pp_b when even.
+    if (ntiles & 1)
+      pv(pp_a, vbuf((ntiles - 1) & 1));
+    else
+      pv(pp_b, vbuf((ntiles - 1) & 1));
   }
 
   // Epilogue: O = O^T / l, rounded to bf16; LSE = m*|scale| + ln l.
@@ -282,7 +336,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_bf16_kernel(PrefillPara
 
 template <int D, bool CAUSAL>
 hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
-  const size_t lds = 2 * PfLayout<D>::STAGE * sizeof(uint16_t);
+  const size_t lds = PfLayout<D>::LDS_BYTES;
   auto kern = prefill_bf16_kernel<D, CAUSAL>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
