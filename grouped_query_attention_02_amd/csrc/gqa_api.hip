@@ -93,6 +93,9 @@ int gqa_prefill(int dtype, const void* q, const void* k, const void* v, void* o,
   const int g = Hq / Hkv;
   if ((long long)S * g > INT_MAX / 2 || (long long)B * S * Hq > (long long)INT_MAX * 64)
     return GQA_ERR_INVALID_ARG;
+  // The bf16 kernel addresses one sequence's K or V rows with 32-bit byte offsets.
+  if (dtype == GQA_DTYPE_BF16 && (long long)S * Hkv * d * 2 > (long long)INT_MAX)
+    return GQA_ERR_UNSUPPORTED;
 
   gqa::PrefillParams p;
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse; p.seqlens = seqlens;
