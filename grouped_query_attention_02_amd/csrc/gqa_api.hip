@@ -105,7 +105,7 @@ int gqa_prefill(int dtype, const void* q, const void* k, const void* v, void* o,
   // that every valid weight rounds to exp2(0) = 1 while masked scores (-inf) give 0.
   p.scale_log2 = fmaxf(p.scale_abs * kLog2e, kMinScaleLog2);
   p.negate_q = softmax_scale < 0.f ? 1 : 0;
-  p.rows_per_wg = dtype == GQA_DTYPE_BF16 ? gqa::prefill_rows_per_wg_bf16()
+  p.rows_per_wg = dtype == GQA_DTYPE_BF16 ? gqa::prefill_rows_per_wg_bf16(d)
                                           : gqa::prefill_rows_per_wg_f32();
   const long long rows = (long long)S * g;
   const long long nrb = (rows + p.rows_per_wg - 1) / p.rows_per_wg;

@@ -50,7 +50,7 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, int causal, hipStream_t s
 hipError_t launch_prefill_f32(const PrefillParams& p, int causal, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeParams& p, bool need_combine, hipStream_t stream);
 
-int prefill_rows_per_wg_bf16();
+int prefill_rows_per_wg_bf16(int d);
 int prefill_rows_per_wg_f32();
 
 }  // namespace gqa

@@ -1,14 +1,14 @@
 // prefill_bf16.hip - bf16 grouped-query attention prefill on gfx950 matrix cores.
 //
-// Work split: one workgroup per (sequence b, K/V head kvh, block of 256 flattened
-// query rows). A flattened row f = i * g + h_local stands for query position i of
-// head kvh * g + h_local, so every row of a block reads the same K/V head
-// (kv_head = q_head / g, blog.gitcode.com "3个GQA核心优化技巧", section
-// "Flash-Attention的稀疏分组优化") and each K/V tile is staged in LDS once and
-// reused by all g heads of the group (same section: K/V reuse in on-chip memory,
-// access granularity raised from a head to a block).
+// Work split: one workgroup per (sequence b, K/V head kvh, block of flattened query
+// rows). A flattened row f = i * g + h_local stands for query position i of head
+// kvh * g + h_local, so every row of a block reads the same K/V head (kv_head = q_head /
+// g, blog.gitcode.com "3个GQA核心优化技巧", section "Flash-Attention的稀疏分组优化") and
+// each K/V tile is staged in LDS once and reused by all g heads of the group (same
+// section: K/V reuse in on-chip memory, access granularity raised from a head to a
+// block).
 //
-// Per K/V tile of 64 keys, each of the 8 waves (32 rows each) computes
+// Per K/V tile of 32 keys, each wave (32 rows) computes
 //   S^T = K Q^T          (A = K rows from LDS, B = Q held in VGPRs)
 //   mask, online softmax with a running max and running sum (webturing.pages.dev
 //   "FlashAttention Serisi", section "Ana fikir": the softmax is accumulated as a
@@ -16,49 +16,50 @@
 //   O^T += V^T P^T       (A = V^T read from row-major LDS with the transposing
 //                        ds_read_b64_tr_b16, B = P taken straight from the score
 //                        accumulators)
-// on v_mfma_f32_32x32x16_bf16. The loop is software-pipelined: iteration t issues the
-// PV product of tile t-1 and the QK^T product of tile t+1 on the matrix cores while the
-// vector ALUs run the softmax of tile t. The running max used as the exponent offset is
-// refreshed only when a row's max grows by more than 2^8 (in exp2 units), so the O
-// rescale is rare; the result is the same normalised softmax because every term of a
-// row always shares one offset. The result equals textbook softmax(scale Q K^T) V over
-// the valid keys (aifullclass.xyz BERT self-attention article, LowRankSelfAttention
+// on v_mfma_f32_32x32x16_bf16. The kernel is kept small (at most 128 VGPRs for d <= 64)
+// so that several waves share each SIMD and the hardware overlaps one wave's matrix
+// products with another wave's softmax. K/V tiles stream from HBM/L2 straight into a
+// 4-slot LDS ring, three tiles ahead of their use. The running max used as the
+// exponent offset is refreshed only when a row's max grows by more than 2^8 (in exp2
+// units), so the O rescale is rare; every term of a row always shares one offset, so
+// the normalised result is unchanged. The result equals textbook softmax(scale Q K^T) V
+// over the valid keys (aifullclass.xyz BERT self-attention article, LowRankSelfAttention
 // example; FlashAttention page FAQ: the computed result is mathematically the same).
 //
 // Masks: key j is visible to query i iff j < L_b and (not causal or j <= i). K/V rows
-// at or past L_b are never read (zero-filled in LDS), so padding may hold anything.
+// at or past L_b are never read (they arrive in LDS as zeros), so padding may hold
+// anything.
 #include "gqa_device.h"
 #include "gqa_kernels.h"
-
-#include <type_traits>
 
 namespace gqa {
 namespace {
 
-constexpr int PF_WAVES = 8;
-constexpr int PF_THREADS = 64 * PF_WAVES;
-constexpr int PF_ROWS = 32 * PF_WAVES;  // flattened query rows per workgroup
-// Keys per K/V tile: 64 for d <= 64, 32 for d = 128 (keeps the score and P registers of
-// two tiles within the 256-VGPR budget of two waves per SIMD).
+constexpr int PF_BN = 32;     // keys per K/V tile
+constexpr int kRing = 4;      // LDS slots per K and per V ring
+constexpr int kAhead = 3;     // tiles in flight ahead of the one being read
+constexpr float kTau = 8.0f;  // exp2 headroom before the running max is refreshed
+
+// Waves per workgroup and workgroups per CU for head size D.
 template <int D>
-constexpr int kBN = D == 128 ? 32 : 64;
-constexpr float kTau = 8.0f;            // exp2 headroom before the running max is refreshed
-constexpr int kNK = 3;                  // K tile ring: K(t+1) read while K(t+2), K(t+3) land
-constexpr int kNV = 4;                  // V tile ring: V(t-1) read while V(t..t+2) land
+struct PfShape {
+  static constexpr int WAVES = D == 128 ? 4 : 8;
+  static constexpr int WG_PER_CU = D == 128 ? 3 : 2;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int ROWS = 32 * WAVES;
+};
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 template <int D>
 struct PfLayout {
-  static constexpr int BN = kBN<D>;
-  static constexpr int NKB = BN / 32;               // 32-key blocks per tile
-  static constexpr int NKS = BN / 16;               // 16-key MFMA steps per tile
-  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
-  static constexpr int ROWB = D * 2;                // bytes per K or V row
-  static constexpr int TILE_B = BN * ROWB;          // bytes per K or V tile
-  static constexpr int NWI = BN * CPR / 64;         // 1 KB DMA wave-instructions per tile
-  static constexpr int LDS_BYTES = (kNK + kNV) * TILE_B;
+  static constexpr int CPR = D / 8;              // 16-byte chunks per row
+  static constexpr int ROWB = D * 2;             // bytes per K or V row
+  static constexpr int TILE_B = PF_BN * ROWB;    // bytes per K or V tile
+  static constexpr int NWI = PF_BN * CPR / 64;   // 1 KB DMA wave-instructions per tile
+  static constexpr int LDS_BYTES = 2 * kRing * TILE_B;
   // Tiles are stored unpadded (DMA writes 1 KB contiguous per wave instruction); the
   // 16-byte chunk q of row r sits at chunk position q ^ f(r). fk makes the K fragment
   // reads (16 rows x one chunk per pass) hit 16 different bank groups; fv does the same
@@ -70,8 +71,6 @@ struct PfLayout {
     return D == 128 ? 4 * (r & 3) : (D == 64 ? 4 * ((r >> 1) & 1) : 0);
   }
 };
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // Buffer resource over [base, base + num_bytes): loads at or past num_bytes return 0.
 __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t num_bytes) {
@@ -95,17 +94,12 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds_ad
                : "memory");
 }
 
-// Wait until at most n of this wave's vector-memory operations are outstanding.
-__device__ __forceinline__ void wait_vm(int n) {
-  switch (n) {
-    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
-    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
-    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
-    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
-    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
-  }
+// Wait until at most n (a compile-time constant) vector-memory operations of this wave
+// are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 __device__ __forceinline__ void block_barrier() {
@@ -115,18 +109,20 @@ __device__ __forceinline__ void block_barrier() {
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(PF_THREADS, 1) void prefill_bf16_kernel(PrefillParams p) {
+__global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WG_PER_CU) void prefill_bf16_kernel(
+    PrefillParams p) {
   using Lay = PfLayout<D>;
-  constexpr int PF_BN = Lay::BN;
-  constexpr int NKB = Lay::NKB, NKS = Lay::NKS;
+  using Shp = PfShape<D>;
+  constexpr int WAVES = Shp::WAVES;
+  constexpr int ROWS = Shp::ROWS;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
-  // LDS: K slots 0..kNK-1, then V slots 0..kNV-1 (byte offsets).
-  auto kslot = [&](int t) { return (t % kNK) * Lay::TILE_B; };
-  auto vslot = [&](int t) { return (kNK + t % kNV) * Lay::TILE_B; };
+  // LDS: K slots 0..kRing-1, then V slots 0..kRing-1 (byte offsets).
+  auto kslot = [](int t) { return (t % kRing) * Lay::TILE_B; };
+  auto vslot = [](int t) { return (kRing + t % kRing) * Lay::TILE_B; };
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
@@ -150,7 +146,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_bf16_kernel(PrefillPara
     Lb = Lb < 0 ? 0 : (Lb > S ? S : Lb);
   }
   const int R = S * g;
-  const int f0 = rb * PF_ROWS;
+  const int f0 = rb * ROWS;
   const int fw = f0 + wave * 32;
   const int f = fw + l32;
   const bool row_ok = f < R;
@@ -161,7 +157,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_bf16_kernel(PrefillPara
   int wave_kv_end = kv_end;        // keys this wave needs
   int wave_mask_from = Lb;         // first key at which some row of the wave is masked
   if (CAUSAL) {
-    const int last_f = min(f0 + PF_ROWS, R) - 1;
+    const int last_f = min(f0 + ROWS, R) - 1;
     kv_end = min(Lb, last_f / g + 1);
     const int wf_last = min(fw + 31, R - 1);
     wave_kv_end = (fw < R) ? min(Lb, wf_last / g + 1) : 0;
@@ -188,61 +184,62 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_bf16_kernel(PrefillPara
   const size_t rstride = (size_t)Hkv * D;  // elements between consecutive keys (BSHD)
   const uint16_t* kbase = static_cast<const uint16_t*>(p.k) + ((size_t)b * S * Hkv + kvh) * D;
   const uint16_t* vbase = static_cast<const uint16_t*>(p.v) + ((size_t)b * S * Hkv + kvh) * D;
+  const uint32_t row_bytes = (uint32_t)(rstride * 2);
 
-  // ---- DMA of one K/V tile pair. A group is this wave's share of K(tk) then V(tv):
-  // wave-instruction k (of 2 * NWI per group) is taken by wave k % 8; k < NWI copies K
-  // chunk block k, otherwise V chunk block k - NWI. Each copy goes through a buffer
-  // resource that ends at row L_b, so rows past the valid range land as zeros and
-  // nothing outside [0, L_b) is ever read.
-  constexpr int kJ = (2 * Lay::NWI + PF_WAVES - 1) / PF_WAVES;
+  // ---- DMA of one K/V tile pair. Wave-instruction k (of 2 * NWI per tile pair) is taken
+  // by wave k % WAVES; k < NWI copies K chunk block k, otherwise V chunk block k - NWI.
+  // Each copy goes through a buffer resource that ends at row L_b, so rows past the valid
+  // range land as zeros and nothing outside [0, L_b) is ever read.
+  // With fewer copies than waves (d = 32) the extra waves repeat a copy (same bytes to
+  // the same place), so every wave issues exactly kJ copies and waits on the same count.
+  constexpr int kCopies = 2 * Lay::NWI;
+  static_assert(kCopies % WAVES == 0 || WAVES % kCopies == 0, "uniform copy count");
+  constexpr int kJ = kCopies >= WAVES ? kCopies / WAVES : 1;  // copies per wave per tile pair
   uint32_t voff[kJ];
-  int n_k = 0, n_v = 0;
+  int kidx[kJ];
 #pragma unroll
   for (int j = 0; j < kJ; ++j) {
-    const int k = wave + PF_WAVES * j;
+    const int k = (wave + WAVES * j) % kCopies;
+    kidx[j] = k;
     const bool is_k = k < Lay::NWI;
-    const int kk = is_k ? k : k - Lay::NWI;
-    const int c = kk * 64 + lane;
+    const int c = (is_k ? k : k - Lay::NWI) * 64 + lane;
     const int row = c / Lay::CPR, pos = c - row * Lay::CPR;
     const int q = pos ^ (is_k ? Lay::fk(row) : Lay::fv(row));
-    voff[j] = (uint32_t)row * (uint32_t)(rstride * 2) + 16u * q;
-    if (k < 2 * Lay::NWI) (is_k ? n_k : n_v) += 1;
+    voff[j] = (uint32_t)row * row_bytes + 16u * q;
   }
-  const int vm_allow = n_v + n_k + n_v;  // group t-1's V part and all of group t
-  const uint32_t row_bytes = (uint32_t)(rstride * 2);
-  auto issue_group = [&](int tk, int tv, bool with_v) {
-    const int tk0 = tk * PF_BN, tv0 = tv * PF_BN;
-    const i32x4 rk = make_rsrc(kbase + (size_t)tk0 * rstride, (uint32_t)max(Lb - tk0, 0) * row_bytes);
-    const i32x4 rv = make_rsrc(vbase + (size_t)tv0 * rstride, (uint32_t)max(Lb - tv0, 0) * row_bytes);
+  auto issue_tile = [&](int t) {
+    const int t0 = t * PF_BN;
+    const uint32_t valid = (uint32_t)max(Lb - t0, 0) * row_bytes;
+    const i32x4 rk = make_rsrc(kbase + (size_t)t0 * rstride, valid);
+    const i32x4 rv = make_rsrc(vbase + (size_t)t0 * rstride, valid);
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {
-      const int k = wave + PF_WAVES * j;
+      const int k = kidx[j];
       if (k < Lay::NWI)
-        dma16(rk, voff[j], lds_base + kslot(tk) + k * 1024);
-      else if (with_v && k < 2 * Lay::NWI)
-        dma16(rv, voff[j], lds_base + vslot(tv) + (k - Lay::NWI) * 1024);
+        dma16(rk, voff[j], lds_base + kslot(t) + k * 1024);
+      else
+        dma16(rv, voff[j], lds_base + vslot(t) + (k - Lay::NWI) * 1024);
     }
   };
 
-  // ---- matrix-core phases
+  // ---- per-tile math
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) oacc[i] = zero16();
 
-  // S^T = K Q^T for two 32-key blocks: lane holds query l32, keys 8(r/4)+4hh+(r%4).
-  // Chunk (2ks + hh) of row kb*32 + l32 sits at position (2ks + hh) ^ fk(l32).
+  // S^T = K Q^T for a 32-key block: lane holds query l32, keys 8(r/4)+4hh+(r%4).
+  // Chunk (2ks + hh) of row l32 sits at position (2ks + hh) ^ fk(l32).
   const int k_lane = l32 * Lay::ROWB + 16 * (hh ^ (Lay::fk(l32) & 1));
   const int k_swz = Lay::fk(l32) & ~1;
-  auto qk = [&](f32x16 (&s)[NKB], int slot_off) {
+  auto qk = [&](int slot_off) {
+    f32x16 s = zero16();
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      const int off = slot_off + k_lane + 16 * ((2 * ks) ^ k_swz);
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(smem + off + kb * 32 * Lay::ROWB);
-        s[kb] = mfma_bf16_32x32x16(as_bf16x8(a), qf[ks], ks == 0 ? zero16() : s[kb]);
-      }
+      const u32x4 a =
+          *reinterpret_cast<const u32x4*>(smem + slot_off + k_lane + 16 * ((2 * ks) ^ k_swz));
+      s = mfma_bf16_32x32x16(as_bf16x8(a), qf[ks], s);
     }
+    return s;
   };
   // O^T += V^T P^T, 16 keys per MFMA; B slot i <-> key 16ks + 8(i/4) + 4hh + (i%4).
   // The transposing read hands lane (group G = lane/16, i = lane%16) keys
@@ -252,9 +249,9 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_bf16_kernel(PrefillPara
   const int tr_q = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // chunk within the 32 columns
   const int v_lane = tr_row * Lay::ROWB + 8 * (lane & 1);
   const int v_swz = Lay::fv(tr_row);  // the same for every (ks, db, +8 rows)
-  auto pv = [&](const bf16x8 (&pp)[NKS], int slot_off) {
+  auto pv = [&](const bf16x8 (&pp)[2], int slot_off) {
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
+    for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
         const int off = slot_off + ks * 16 * Lay::ROWB + v_lane + 16 * ((4 * db + tr_q) ^ v_swz);
@@ -272,41 +269,43 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_bf16_kernel(PrefillPara
   float m_run = -INFINITY, l_run = 0.f;
   const float c = p.scale_log2;
 
-  // Key j = t0 + kb*32 + 8(r/4) + 4hh + (r%4) is kept iff j < lim: the sign of j - lim
-  // selects between the score and -inf bit patterns (no compare masks in SGPRs).
-  auto mask = [&](f32x16 (&s)[NKB], int t0) {
-    const int base = t0 + 4 * hh - lim;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+  auto tile = [&](int t) {
+    f32x16 s = qk(kslot(t));
+    const int t0 = t * PF_BN;
+    if (t0 + PF_BN > wave_mask_from) {
+      // Key j = t0 + 8(r/4) + 4hh + (r%4) is kept iff j < lim: the sign of j - lim selects
+      // between the score and -inf bit patterns (no compare masks in SGPRs).
+      const int base = t0 + 4 * hh - lim;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const uint32_t keep = (uint32_t)((base + kb * 32 + 8 * (r >> 2) + (r & 3)) >> 31);
-        s[kb][r] = __uint_as_float((__float_as_uint(s[kb][r]) & keep) | (0xff800000u & ~keep));
+        const uint32_t keep = (uint32_t)((base + 8 * (r >> 2) + (r & 3)) >> 31);
+        s[r] = __uint_as_float((__float_as_uint(s[r]) & keep) | (0xff800000u & ~keep));
       }
-  };
-  // Returns this lane's rescale factor for O; P goes to pp as bf16.
-  auto softmax = [&](f32x16 (&s)[NKB], bf16x8 (&pp)[NKS]) -> float {
+    }
     float mx = m_run;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, xor32(mx));  // the other 32 keys of this row sit in lane l ^ 32
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = pair_max(mx);  // the other 16 keys of this row sit in lane l ^ 32
     const bool fresh = m_run == -INFINITY;
     const bool refresh = fresh ? (mx != -INFINITY) : ((mx - m_run) * c > kTau);
-    const float m_new = refresh ? mx : m_run;
-    const float alpha = refresh ? (fresh ? 0.f : fast_exp2((m_run - m_new) * c)) : 1.f;
-    m_run = m_new;
-    const float msc = (m_new == -INFINITY ? 0.f : m_new) * c;
+    if (wave_any(refresh)) {
+      const float m_new = refresh ? mx : m_run;
+      const float alpha = refresh ? (fresh ? 0.f : fast_exp2((m_run - m_new) * c)) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      m_run = m_new;
+    }
+    const float msc = (m_run == -INFINITY ? 0.f : m_run) * c;
+    bf16x8 pp[2];
     float lsum = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const int kb = ks >> 1, r0 = 8 * (ks & 1);
+    for (int ks = 0; ks < 2; ++ks) {
       float e[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        e[i] = fast_exp2(fmaf(s[kb][r0 + i], c, -msc));  // masked: exp2(-inf) = 0 as c > 0
-      }
+      for (int i = 0; i < 8; ++i) e[i] = fast_exp2(fmaf(s[8 * ks + i], c, -msc));  // exp2(-inf) = 0
       u32x4 u;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -315,82 +314,28 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_bf16_kernel(PrefillPara
       }
       pp[ks] = as_bf16x8(u);
     }
-    l_run = l_run * alpha + lsum;
-    return alpha;
-  };
-  auto rescale = [&](float alpha) {
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    l_run += lsum;
+    pv(pp, vslot(t));
   };
 
-  // ---- pipeline: iteration t runs PV(t-1), QK(t+1) and softmax(t) while the DMA of
-  // K(t+3) and V(t+2) is in flight (K(t+1), V(t-1) are read; K(t+2), V(t), V(t+1) may
-  // still be landing). Every wave runs every tile of the workgroup (tiles past a causal
-  // wave's rows are fully masked and add nothing); the QK of the last iteration reads a
-  // tile that is not used. The loop is unrolled by two with the register roles swapped,
-  // so no accumulator is ever copied.
-  f32x16 s_a[NKB], s_b[NKB];
-  bf16x8 pp_a[NKS], pp_b[NKS];
+  // ---- pipeline: the DMA of tile t+3 is issued before tile t is computed; after tile t
+  // each wave waits for its own copies of tile t+1 and the barrier publishes everyone's.
   if (ntiles > 0) {
-    issue_group(0, 0, false);
-    issue_group(1, 0, true);
-    issue_group(2, 1, true);
-    wait_vm(0);
+#pragma unroll
+    for (int t = 0; t < kAhead; ++t) issue_tile(t);
+    wait_vm<kJ * (kAhead - 1)>();  // tile 0 has landed
   }
   block_barrier();
-  if (ntiles > 0) qk(s_a, kslot(0));
-  block_barrier();  // every wave has read K(0) before K(3) replaces it
-
-  auto step = [&](auto do_pv, int t, f32x16 (&s_cur)[NKB], f32x16 (&s_nxt)[NKB],
-                  bf16x8 (&pp_prev)[NKS], bf16x8 (&pp_cur)[NKS]) {
-    __builtin_amdgcn_sched_barrier(0);
-    issue_group(t + 3, t + 2, true);
-    if (t * PF_BN + PF_BN > wave_mask_from) mask(s_cur, t * PF_BN);
-    __builtin_amdgcn_sched_barrier(0);
-    // One scheduling region: matrix-core products of tiles t-1 and t+1 interleaved with
-    // the vector-ALU softmax of tile t (each MFMA is followed by a slice of the VALU work).
-    constexpr bool kPV = decltype(do_pv)::value;
-    if constexpr (kPV) pv(pp_prev, vslot(t - 1));
-    qk(s_nxt, kslot(t + 1));
-    const float alpha = softmax(s_cur, pp_cur);
-    constexpr int kMfma = (kPV ? NKS * (D / 32) : 0) + NKB * (D / 16);
-    constexpr int kValuPer = (kMfma >= 32 ? 4 : (kMfma >= 16 ? 7 : 14));
-#pragma unroll
-    for (int i = 0; i < kMfma; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, kValuPer, 0);
-    }
-    // Pin P(t) here: without a use inside the region the compiler sinks the exponentials
-    // into the next step, next to their consumer, and nothing overlaps the MFMAs.
-#pragma unroll
-    for (int i = 0; i < NKS; ++i) asm volatile("" ::"v"(pp_cur[i]));
-    __builtin_amdgcn_sched_barrier(0);
-    if (wave_any(alpha != 1.f)) rescale(alpha);  // after PV(t-1), before PV(t)
-    wait_vm(vm_allow);  // this wave's copies of K(t+2) and V(t) have landed
-    block_barrier();    // ... and every other wave's
-  };
-  using no_pv = std::integral_constant<bool, false>;
-  using with_pv = std::integral_constant<bool, true>;
-  int t = 1;
-  if (ntiles > 0) {
-    step(no_pv{}, 0, s_a, s_b, pp_b, pp_a);
-    for (; t + 1 < ntiles; t += 2) {
-      step(with_pv{}, t, s_b, s_a, pp_a, pp_b);
-      step(with_pv{}, t + 1, s_a, s_b, pp_b, pp_a);
-    }
-    if (t < ntiles) step(with_pv{}, t, s_b, s_a, pp_a, pp_b);
-    // PV of the last tile: its P sits in pp_a when ntiles is odd, pp_b when even.
-    if (ntiles & 1)
-      pv(pp_a, vslot(ntiles - 1));
-    else
-      pv(pp_b, vslot(ntiles - 1));
-    wait_vm(0);  // drain the copies issued for tiles past the end
+  for (int t = 0; t < ntiles; ++t) {
+    issue_tile(t + kAhead);  // past the end: empty resource, zeros land in a free slot
+    if (t < wave_nt) tile(t);
+    wait_vm<kJ * kAhead - kJ>();  // this wave's copies of tile t+1 have landed
+    block_barrier();              // ... and every wave's; slot t may be overwritten next
   }
+  if (ntiles > 0) wait_vm<0>();  // drain the copies issued for tiles past the end
 
   // Epilogue: O = O^T / l, rounded to bf16; LSE = m*|scale| + ln l.
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (row_ok) {
     uint16_t* orow = static_cast<uint16_t*>(p.o) + (((size_t)b * S + qi) * Hq + hq) * D;
@@ -417,13 +362,15 @@ hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(8 * p.per_xcd), dim3(PF_THREADS), lds, stream, p);
+  hipLaunchKernelGGL(kern, dim3(8 * p.per_xcd), dim3(PfShape<D>::THREADS), lds, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int prefill_rows_per_wg_bf16() { return PF_ROWS; }
+int prefill_rows_per_wg_bf16(int d) {
+  return d == 128 ? PfShape<128>::ROWS : (d == 64 ? PfShape<64>::ROWS : PfShape<32>::ROWS);
+}
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, int causal, hipStream_t stream) {
   switch (p.d) {
