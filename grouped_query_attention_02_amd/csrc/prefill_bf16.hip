@@ -8,7 +8,7 @@
 // section: K/V reuse in on-chip memory, access granularity raised from a head to a
 // block).
 //
-// Per K/V tile of 32 keys, each wave (32 rows) computes
+// Per K/V tile (64 keys, 32 for d = 128), each wave (32 rows) computes
 //   S^T = K Q^T          (A = K rows from LDS, B = Q held in VGPRs)
 //   mask, online softmax with a running max and running sum (webturing.pages.dev
 //   "FlashAttention Serisi", section "Ana fikir": the softmax is accumulated as a
@@ -35,7 +35,6 @@
 namespace gqa {
 namespace {
 
-constexpr int PF_BN = 32;     // keys per K/V tile
 constexpr int kRing = 4;      // LDS slots per K and per V ring
 constexpr int kAhead = 3;     // tiles in flight ahead of the one being read
 constexpr float kTau = 8.0f;  // exp2 headroom before the running max is refreshed
@@ -43,6 +42,8 @@ constexpr float kTau = 8.0f;  // exp2 headroom before the running max is refresh
 // Waves per workgroup and workgroups per CU for head size D.
 template <int D>
 struct PfShape {
+  // Keys per K/V tile: 64 while the registers allow four waves per SIMD, 32 for d = 128.
+  static constexpr int BN = D == 128 ? 32 : 64;
   static constexpr int WAVES = D == 128 ? 4 : 8;
   static constexpr int WG_PER_CU = D == 128 ? 3 : 2;
   static constexpr int THREADS = 64 * WAVES;
@@ -55,10 +56,13 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 template <int D>
 struct PfLayout {
+  static constexpr int BN = PfShape<D>::BN;
+  static constexpr int NKB = BN / 32;            // 32-key score blocks per tile
+  static constexpr int NKS = BN / 16;            // 16-key MFMA steps per tile
   static constexpr int CPR = D / 8;              // 16-byte chunks per row
   static constexpr int ROWB = D * 2;             // bytes per K or V row
-  static constexpr int TILE_B = PF_BN * ROWB;    // bytes per K or V tile
-  static constexpr int NWI = PF_BN * CPR / 64;   // 1 KB DMA wave-instructions per tile
+  static constexpr int TILE_B = BN * ROWB;       // bytes per K or V tile
+  static constexpr int NWI = BN * CPR / 64;      // 1 KB DMA wave-instructions per tile
   static constexpr int LDS_BYTES = 2 * kRing * TILE_B;
   // Tiles are stored unpadded (DMA writes 1 KB contiguous per wave instruction); the
   // 16-byte chunk q of row r sits at chunk position q ^ f(r). fk makes the K fragment
@@ -115,6 +119,8 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WG_PER_CU) void pr
   using Shp = PfShape<D>;
   constexpr int WAVES = Shp::WAVES;
   constexpr int ROWS = Shp::ROWS;
+  constexpr int PF_BN = Lay::BN;
+  constexpr int NKB = Lay::NKB, NKS = Lay::NKS;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
   // LDS: K slots 0..kRing-1, then V slots 0..kRing-1 (byte offsets).
@@ -231,15 +237,18 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WG_PER_CU) void pr
   // Chunk (2ks + hh) of row l32 sits at position (2ks + hh) ^ fk(l32).
   const int k_lane = l32 * Lay::ROWB + 16 * (hh ^ (Lay::fk(l32) & 1));
   const int k_swz = Lay::fk(l32) & ~1;
-  auto qk = [&](int slot_off) {
-    f32x16 s = zero16();
+  auto qk = [&](f32x16 (&s)[NKB], int slot_off) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = zero16();
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      const u32x4 a =
-          *reinterpret_cast<const u32x4*>(smem + slot_off + k_lane + 16 * ((2 * ks) ^ k_swz));
-      s = mfma_bf16_32x32x16(as_bf16x8(a), qf[ks], s);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(smem + slot_off + kb * 32 * Lay::ROWB +
+                                                        k_lane + 16 * ((2 * ks) ^ k_swz));
+        s[kb] = mfma_bf16_32x32x16(as_bf16x8(a), qf[ks], s[kb]);
+      }
     }
-    return s;
   };
   // O^T += V^T P^T, 16 keys per MFMA; B slot i <-> key 16ks + 8(i/4) + 4hh + (i%4).
   // The transposing read hands lane (group G = lane/16, i = lane%16) keys
@@ -249,9 +258,9 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WG_PER_CU) void pr
   const int tr_q = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // chunk within the 32 columns
   const int v_lane = tr_row * Lay::ROWB + 8 * (lane & 1);
   const int v_swz = Lay::fv(tr_row);  // the same for every (ks, db, +8 rows)
-  auto pv = [&](const bf16x8 (&pp)[2], int slot_off) {
+  auto pv = [&](const bf16x8 (&pp)[NKS], int slot_off) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
         const int off = slot_off + ks * 16 * Lay::ROWB + v_lane + 16 * ((4 * db + tr_q) ^ v_swz);
@@ -270,22 +279,27 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WG_PER_CU) void pr
   const float c = p.scale_log2;
 
   auto tile = [&](int t) {
-    f32x16 s = qk(kslot(t));
+    f32x16 s[NKB];
+    qk(s, kslot(t));
     const int t0 = t * PF_BN;
     if (t0 + PF_BN > wave_mask_from) {
-      // Key j = t0 + 8(r/4) + 4hh + (r%4) is kept iff j < lim: the sign of j - lim selects
-      // between the score and -inf bit patterns (no compare masks in SGPRs).
+      // Key j = t0 + 32kb + 8(r/4) + 4hh + (r%4) is kept iff j < lim: the sign of j - lim
+      // selects between the score and -inf bit patterns (no compare masks in SGPRs).
       const int base = t0 + 4 * hh - lim;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const uint32_t keep = (uint32_t)((base + 8 * (r >> 2) + (r & 3)) >> 31);
-        s[r] = __uint_as_float((__float_as_uint(s[r]) & keep) | (0xff800000u & ~keep));
-      }
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t keep = (uint32_t)((base + 32 * kb + 8 * (r >> 2) + (r & 3)) >> 31);
+          s[kb][r] = __uint_as_float((__float_as_uint(s[kb][r]) & keep) | (0xff800000u & ~keep));
+        }
     }
     float mx = m_run;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-    mx = pair_max(mx);  // the other 16 keys of this row sit in lane l ^ 32
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = pair_max(mx);  // the other keys of this row sit in lane l ^ 32
     const bool fresh = m_run == -INFINITY;
     const bool refresh = fresh ? (mx != -INFINITY) : ((mx - m_run) * c > kTau);
     if (wave_any(refresh)) {
@@ -299,13 +313,14 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WG_PER_CU) void pr
       m_run = m_new;
     }
     const float msc = (m_run == -INFINITY ? 0.f : m_run) * c;
-    bf16x8 pp[2];
+    bf16x8 pp[NKS];
     float lsum = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < NKS; ++ks) {
       float e[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) e[i] = fast_exp2(fmaf(s[8 * ks + i], c, -msc));  // exp2(-inf) = 0
+      for (int i = 0; i < 8; ++i)
+        e[i] = fast_exp2(fmaf(s[ks >> 1][8 * (ks & 1) + i], c, -msc));  // exp2(-inf) = 0
       u32x4 u;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
