@@ -12,6 +12,8 @@ steps, the causal Llama-style prefill and the uniform 8k decode are timed the sa
 and reported under `also` (not part of `value`).
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --only prefill|decode|copy --steps K     (work for rocprofv3 runs)
+    python bench.py --summarize-kernels DIR | --summarize-pmc DIR
 """
 from __future__ import annotations
 
@@ -136,6 +138,91 @@ def _cpu_baseline(pc, target_s: float):
                       f"its {total_rows} rows), fp64, {dt:.1f} s wall"}
 
 
+def _only(what, steps, dev):
+    """Run one piece of work `steps` times (for rocprofv3 runs) and exit."""
+    import torch
+    import workloads as W
+    if what == "prefill":
+        c = _prefill_case(W.WORKLOADS["bert_base_prefill"], dev)
+        fn = lambda: _run_prefill(c)
+    elif what == "decode":
+        c = _decode_case(W.WORKLOADS["mqa_ragged_decode"], dev)
+        fn = lambda: _run_decode(c)
+    else:  # a plain device copy of known size, to calibrate the HBM byte counters
+        n = 256 << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        fn = lambda: dst.copy_(src)
+        print(f"[bench] copy of {n} bytes per launch", file=sys.stderr)
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    print(f"[bench] ran {what} x{steps}", file=sys.stderr, flush=True)
+    return 0
+
+
+def _csv_rows(d, name):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", name), recursive=True)):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _summarize_kernels(d):
+    """Per-kernel call count and mean/min duration (us) from rocprofv3 kernel traces."""
+    rows = _csv_rows(d, "*kernel_trace.csv")
+    acc = {}
+    for r in rows:
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        acc.setdefault(r["Kernel_Name"], []).append(dur)
+    for name, v in sorted(acc.items(), key=lambda kv: -sum(kv[1])):
+        print(f"{len(v):5d} calls  mean {statistics.mean(v):10.2f} us  min {min(v):10.2f} us"
+              f"  total {sum(v):11.1f} us  {name[:110]}")
+    return 0
+
+
+def _summarize_pmc(d):
+    """Per-kernel mean of each counter (summed over its instances) from rocprofv3 --pmc."""
+    rows = _csv_rows(d, "*counter_collection.csv")
+    per = {}
+    for r in rows:
+        key = (r["Kernel_Name"], r["Counter_Name"], r["Dispatch_Id"])
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    agg = {}
+    for (kname, cname, _), v in per.items():
+        agg.setdefault((kname, cname), []).append(v)
+    for (kname, cname), v in sorted(agg.items()):
+        print(f"{cname:28s} mean {statistics.mean(v):14.6g}  n={len(v):3d}  {kname[:100]}")
+    return 0
+
+
+def _recorded_traffic(summary_name, source_name):
+    """HBM bytes per launch recorded in profiles/<summary_name>, or None when the kernel
+    source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", summary_name)
+    src = os.path.join(ROOT, "grouped_query_attention_02_amd", "csrc", source_name)
+    if not (os.path.exists(path) and os.path.exists(src)):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith(("#", " ", "`")):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    with open(src, "rb") as fh:
+        digest = hashlib.sha256(fh.read()).hexdigest()
+    if fields.get("kernel_source_sha256") != digest:
+        return None
+    try:
+        return int(float(fields["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,7 +231,18 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the extra workloads")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--only", choices=["prefill", "decode", "copy"],
+                    help="profiling run: execute just this work --steps times and exit")
+    ap.add_argument("--summarize-kernels", metavar="DIR",
+                    help="print per-kernel mean durations from rocprofv3 --kernel-trace CSV output")
+    ap.add_argument("--summarize-pmc", metavar="DIR",
+                    help="print per-kernel mean counter values from rocprofv3 --pmc CSV output")
     args = ap.parse_args(argv)
+
+    if args.summarize_kernels:
+        return _summarize_kernels(args.summarize_kernels)
+    if args.summarize_pmc:
+        return _summarize_pmc(args.summarize_pmc)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -162,6 +260,9 @@ def main(argv=None):
     gqa.load()
     dev = torch.device("cuda:0")
     print(f"[bench] device {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
+
+    if args.only:
+        return _only(args.only, args.steps, dev)
 
     pc = _prefill_case(W.WORKLOADS["bert_base_prefill"], dev)
     dc = _decode_case(W.WORKLOADS["mqa_ragged_decode"], dev)
@@ -254,8 +355,9 @@ def main(argv=None):
         "roofline": {
             "bound": "mfma", "achieved": round(p_tflops, 3),
             "peak": perfmodel.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(p_tflops / perfmodel.PEAK_BF16_TFLOPS, 4), "traffic": None,
-            "kernel": "prefill_bf16_kernel<64, non-causal>",
+            "frac": round(p_tflops / perfmodel.PEAK_BF16_TFLOPS, 4),
+            "traffic": _recorded_traffic("prefill_bert_base_traffic.md", "prefill_bf16.hip"),
+            "kernel": "prefill_bf16_kernel<64, false>",
             "launch_us_mean": round(p_avg * 1e3, 2), "flops_per_launch": pc["flops"],
         },
         "decode": {
