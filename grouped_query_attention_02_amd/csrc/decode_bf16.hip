@@ -45,7 +45,8 @@ __device__ __forceinline__ int clamp_len(const int32_t* lens, int b, int cap) {
 
 __device__ __forceinline__ int tiles_of(int L) { return (L + DC_TILE - 1) / DC_TILE; }
 
-// Sum of an int over the workgroup (all threads get the result).
+// Sum over a workgroup of NT threads (all threads get the result).
+template <int NT>
 __device__ long long block_sum(long long v, long long* scratch) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
@@ -55,19 +56,20 @@ __device__ long long block_sum(long long v, long long* scratch) {
   __syncthreads();
   long long t = 0;
 #pragma unroll
-  for (int w = 0; w < DC_WAVES; ++w) t += scratch[w];
+  for (int w = 0; w < NT / 64; ++w) t += scratch[w];
   return t;
 }
 
 // Tiles of sequences [0, B) (per K/V unit of one sequence) and of [0, b_end).
+template <int NT>
 __device__ void tile_prefix(const int32_t* lens, int B, int cap, int b_end, long long* total,
                             long long* before, long long* scratch) {
   long long tot = 0, bef = 0;
-  for (int base = 0; base < B; base += DC_THREADS) {
+  for (int base = 0; base < B; base += NT) {
     const int bb = base + threadIdx.x;
     const long long tb = bb < B ? tiles_of(clamp_len(lens, bb, cap)) : 0;
-    tot += block_sum(tb, scratch);
-    bef += block_sum(bb < b_end ? tb : 0, scratch);
+    tot += block_sum<NT>(tb, scratch);
+    bef += block_sum<NT>(bb < b_end ? tb : 0, scratch);
   }
   *total = tot;
   *before = bef;
@@ -122,6 +124,8 @@ template <int D>
 struct DcLayout {
   static constexpr int OSTR = D + 4;  // floats per query row of a wave's O in LDS
   static constexpr int O_FLOATS = DC_WAVES * 32 * OSTR;
+  static constexpr int QSTR = D + 8;  // bf16 per query row of Q in LDS (conflict-free reads)
+  static constexpr int Q_BYTES = 32 * QSTR * 2;
 };
 
 template <int D>
@@ -129,8 +133,9 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_split_kernel(DecodeParam
   constexpr int DPL = D / 32;  // output columns per lane in the V^T operand
   using Lay = DcLayout<D>;
   extern __shared__ __attribute__((aligned(16))) float dsm[];
-  float* s_o = dsm;                        // [wave][32][OSTR]
-  float* s_m = dsm + Lay::O_FLOATS;        // [wave][32]
+  uint16_t* s_q = reinterpret_cast<uint16_t*>(dsm);                       // [32][QSTR] bf16
+  float* s_o = dsm + Lay::Q_BYTES / 4;     // [wave][32][OSTR]
+  float* s_m = s_o + Lay::O_FLOATS;        // [wave][32]
   float* s_l = s_m + DC_WAVES * 32;        // [wave][32]
   long long* scratch = reinterpret_cast<long long*>(s_l + DC_WAVES * 32);  // 8 entries
 
@@ -145,7 +150,7 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_split_kernel(DecodeParam
   const float c = p.scale_log2;
 
   long long T, unused;
-  tile_prefix(p.lens, p.B, cap, 0, &T, &unused, scratch);
+  tile_prefix<DC_THREADS>(p.lens, p.B, cap, 0, &T, &unused, scratch);
   T *= HU;
   // Never more shares than tiles, so every share is non-empty and the shares
   // overlapping a unit form one run of consecutive workgroups.
@@ -179,17 +184,6 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_split_kernel(DecodeParam
     const int nh = min(32, p.g - qb * 32);
     const int u = (b * p.Hkv + kvh) * p.nqb + qb;
 
-    // Q^T (B operand): lane holds head hbase + l32, d = ks*16 + hh*8 .. +7.
-    bf16x8 qf[D / 16];
-    {
-      const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + ((size_t)b * p.Hq + hbase + l32) * D;
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        u32x4 v = l32 < nh ? ldg16(qrow + ks * 16 + hh * 8) : zero_u32x4();
-        v[0] ^= flip; v[1] ^= flip; v[2] ^= flip; v[3] ^= flip;
-        qf[ks] = as_bf16x8(v);
-      }
-    }
     const size_t cache_off = ((size_t)(b * p.Hkv + kvh) * cap) * D;
     const uint16_t* kb_ = static_cast<const uint16_t*>(p.kc) + cache_off;
     const uint16_t* vb_ = static_cast<const uint16_t*>(p.vc) + cache_off;
@@ -199,48 +193,86 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_split_kernel(DecodeParam
     for (int i = 0; i < DPL; ++i) oacc[i] = zero16();
     float m_run = -INFINITY, l_run = 0.f;
 
-    for (int tt = ta + wave; tt < te; tt += DC_WAVES) {
-      const int j0 = tt * DC_TILE;
-      // K rows (A operand): lane reads 16 bytes of row j0 + l32.
+    // One tile's K rows (A operand: lane reads 16 bytes of row j0 + l32) and V rows (for
+    // 16-key step ks2 and slot i, key j0 + 16ks2 + 8(i/4) + 4hh + (i%4); the lane reads DPL
+    // consecutive values starting at d = DPL * l32). Loads go through a buffer resource that
+    // starts at the tile and ends at row L_b, so rows at or past L_b read as zeros, the lane
+    // offsets are the same for every tile and no load needs a predicate.
+    struct TileRegs {
       u32x4 kf[D / 16];
-      const int jk = j0 + l32;
+      uint32_t vl[2][8][DPL / 2];
+    };
+    const uint32_t row_b = D * 2;
+    const uint32_t k_lane = l32 * row_b + hh * 16;
+    const uint32_t v_lane = (4 * hh) * row_b + DPL * 2 * l32;
+    auto rsrc = [&](const uint16_t* base, int tt) {
+      const int j0 = tt * DC_TILE;
+      const uint32_t valid = (uint32_t)max(Lb - j0, 0) * row_b;
+      return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)j0 * D), 0, valid, 0x00020000);
+    };
+    auto load_k = [&](TileRegs& r, int tt) {
+      const __amdgpu_buffer_rsrc_t rk = rsrc(kb_, tt);
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks)
-        kf[ks] = jk < Lb ? ldg16(kb_ + (size_t)jk * D + ks * 16 + hh * 8) : zero_u32x4();
-      // V rows: for 16-key step ks2 and slot i, key j0 + 16ks2 + 8(i/4) + 4hh + (i%4);
-      // the lane reads DPL consecutive values starting at d = DPL * l32.
-      uint32_t vl[2][8][DPL / 2];
+        r.kf[ks] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_lane + ks * 32, 0, 0));
+    };
+    auto load_v = [&](TileRegs& r, int tt) {
+      const __amdgpu_buffer_rsrc_t rv = rsrc(vb_, tt);
 #pragma unroll
       for (int ks2 = 0; ks2 < 2; ++ks2)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const int jv = j0 + 16 * ks2 + 8 * (i >> 2) + 4 * hh + (i & 3);
-          const uint16_t* src = vb_ + (size_t)jv * D + DPL * l32;
+          const uint32_t off = v_lane + (16 * ks2 + 8 * (i >> 2) + (i & 3)) * row_b;
           if constexpr (DPL == 4) {
-            const u32x2 x = jv < Lb ? ldg8(src) : u32x2{0u, 0u};
-            vl[ks2][i][0] = x[0];
-            vl[ks2][i][1] = x[1];
+            const u32x2 x =
+                __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, off, 0, 0));
+            r.vl[ks2][i][0] = x[0];
+            r.vl[ks2][i][1] = x[1];
           } else {
-            vl[ks2][i][0] = jv < Lb ? *reinterpret_cast<const uint32_t*>(src) : 0u;
+            r.vl[ks2][i][0] = __builtin_amdgcn_raw_buffer_load_b32(rv, off, 0, 0);
           }
         }
-
+    };
+    TileRegs r0;
+    // Q of the block's heads -> LDS (rows past nh are zeros); the B operand of S^T = K Q^T
+    // is read back per tile: lane holds head l32, d = ks*16 + hh*8 .. +7. The wave's first
+    // K/V tile is requested before the Q staging so both round trips overlap.
+    if (ta + wave < te) {
+      load_k(r0, ta + wave);
+      load_v(r0, ta + wave);
+    }
+    {
+      const uint16_t* qsrc = static_cast<const uint16_t*>(p.q) + ((size_t)b * p.Hq + hbase) * D;
+      for (int ci = tid; ci < 32 * (D / 8); ci += DC_THREADS) {
+        const int row = ci / (D / 8), col = ci - row * (D / 8);
+        u32x4 v = row < nh ? ldg16(qsrc + (size_t)row * D + col * 8) : zero_u32x4();
+        v[0] ^= flip; v[1] ^= flip; v[2] ^= flip; v[3] ^= flip;
+        *reinterpret_cast<u32x4*>(s_q + row * Lay::QSTR + col * 8) = v;
+      }
+    }
+    __syncthreads();
+    auto compute_tile = [&](TileRegs& r, int tt, bool more) {
+      const int j0 = tt * DC_TILE;
       f32x16 s = zero16();
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) s = mfma_bf16_32x32x16(as_bf16x8(kf[ks]), qf[ks], s);
-
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const u32x4 qv = *reinterpret_cast<const u32x4*>(s_q + l32 * Lay::QSTR + ks * 16 + hh * 8);
+        s = mfma_bf16_32x32x16(as_bf16x8(r.kf[ks]), as_bf16x8(qv), s);
+      }
+      if (more) load_k(r, tt + DC_WAVES);  // K registers are free again: fetch the next tile
       const bool need_mask = j0 + DC_TILE > Lb;
       if (need_mask) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = j0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (j >= Lb) s[r] = -INFINITY;
+        for (int rr = 0; rr < 16; ++rr) {
+          const int j = j0 + 8 * (rr >> 2) + 4 * hh + (rr & 3);
+          if (j >= Lb) s[rr] = -INFINITY;
         }
       }
       float mx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-      mx = fmaxf(mx, xor32(mx));
+      for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[rr]);
+      mx = pair_max(mx);
       const float m_new = fmaxf(m_run, mx);
       if (wave_any(m_new > m_run)) {
         const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_new) * c);
@@ -248,23 +280,22 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_split_kernel(DecodeParam
 #pragma unroll
         for (int i = 0; i < DPL; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+          for (int rr = 0; rr < 16; ++rr) oacc[i][rr] *= alpha;
         m_run = m_new;
       }
       const float msc = (m_run == -INFINITY ? 0.f : m_run) * c;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pv = fast_exp2(fmaf(s[r], c, -msc));
-        if (need_mask) pv = (s[r] == -INFINITY) ? 0.f : pv;
-        s[r] = pv;
+      for (int rr = 0; rr < 16; ++rr) {
+        float pv = fast_exp2(fmaf(s[rr], c, -msc));
+        if (need_mask) pv = (s[rr] == -INFINITY) ? 0.f : pv;
+        s[rr] = pv;
         l_run += pv;
       }
-
 #pragma unroll
       for (int ks2 = 0; ks2 < 2; ++ks2) {
-        const int r0 = 8 * ks2;
-        const bf16x8 pb = pack_bf16x8(s[r0 + 0], s[r0 + 1], s[r0 + 2], s[r0 + 3], s[r0 + 4],
-                                      s[r0 + 5], s[r0 + 6], s[r0 + 7]);
+        const int e0 = 8 * ks2;
+        const bf16x8 pb = pack_bf16x8(s[e0 + 0], s[e0 + 1], s[e0 + 2], s[e0 + 3], s[e0 + 4],
+                                      s[e0 + 5], s[e0 + 6], s[e0 + 7]);
 #pragma unroll
         for (int cc = 0; cc < DPL; ++cc) {
           const int word = cc >> 1;       // which dword of the lane's DPL values
@@ -272,16 +303,21 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_split_kernel(DecodeParam
           u32x4 a;
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
-            const uint32_t x0 = vl[ks2][2 * jj][word], x1 = vl[ks2][2 * jj + 1][word];
+            const uint32_t x0 = r.vl[ks2][2 * jj][word], x1 = r.vl[ks2][2 * jj + 1][word];
             a[jj] = upper ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
           }
           oacc[cc] = mfma_bf16_32x32x16(as_bf16x8(a), pb, oacc[cc]);
         }
       }
-    }
+      if (more) load_v(r, tt + DC_WAVES);  // V registers are free again
+    };
+
+    // The wave's tiles are ta + wave, ta + wave + 4, ...; each tile's K (V) registers are
+    // refilled with the next tile's rows as soon as QK^T (PV) has consumed them.
+    for (int tt = ta + wave; tt < te; tt += DC_WAVES) compute_tile(r0, tt, tt + DC_WAVES < te);
 
     // Merge the waves' running states through LDS.
-    const float l_tot = l_run + xor32(l_run);
+    const float l_tot = pair_sum(l_run);
     if (hh == 0) {
       s_m[wave * 32 + l32] = m_run;
       s_l[wave * 32 + l32] = l_tot;
@@ -352,11 +388,14 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_split_kernel(DecodeParam
 // Merge the split partials of one unit (b, kvh, query block): workgroup (u, head block),
 // one thread per (head, 4 output columns). Partials are visited in workgroup order with
 // a running max, so the merge order is fixed and the result deterministic.
+constexpr int CB_THREADS = 64;  // one wave per combine workgroup
+constexpr int CB_BATCH = 16;    // partials whose loads are issued together
+
 template <int D>
-__global__ __launch_bounds__(DC_THREADS) void decode_combine_kernel(DecodeParams p) {
+__global__ __launch_bounds__(CB_THREADS) void decode_combine_kernel(DecodeParams p) {
   constexpr int TPH = D / 4;              // threads per head
-  constexpr int HPB = DC_THREADS / TPH;   // heads per workgroup
-  __shared__ long long scratch[DC_WAVES + 2];
+  constexpr int HPB = CB_THREADS / TPH;   // heads per workgroup
+  __shared__ long long scratch[CB_THREADS / 64];
   const int u = blockIdx.x;
   const int qb = u % p.nqb;
   const int kvh = (u / p.nqb) % p.Hkv;
@@ -364,7 +403,7 @@ __global__ __launch_bounds__(DC_THREADS) void decode_combine_kernel(DecodeParams
   const int cap = p.max_len;
   const long long HU = (long long)p.Hkv * p.nqb;
   long long T, before;
-  tile_prefix(p.lens, p.B, cap, b, &T, &before, scratch);
+  tile_prefix<CB_THREADS>(p.lens, p.B, cap, b, &T, &before, scratch);
   T *= HU;
   const int Tb = tiles_of(clamp_len(p.lens, b, cap));
   const int hbase = kvh * p.g + qb * 32;
@@ -388,11 +427,11 @@ __global__ __launch_bounds__(DC_THREADS) void decode_combine_kernel(DecodeParams
   if (wa == wb) return;  // one workgroup covered the unit and wrote the output
 
   float m = -INFINITY, den = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = wa; s0 <= wb; s0 += 8) {
-    float lw[8];
-    u32x4 ov[8];
+  for (int s0 = wa; s0 <= wb; s0 += CB_BATCH) {
+    float lw[CB_BATCH];
+    u32x4 ov[CB_BATCH];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < CB_BATCH; ++k) {
       const int s = s0 + k;
       if (s <= wb) {
         const size_t slot = (size_t)s + u;
@@ -404,7 +443,7 @@ __global__ __launch_bounds__(DC_THREADS) void decode_combine_kernel(DecodeParams
       }
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < CB_BATCH; ++k) {
       if (lw[k] == -INFINITY) continue;
       const float m_new = fmaxf(m, lw[k]);
       const float sc = (m == -INFINITY) ? 0.f : fast_exp2((m - m_new) * kLog2e);
@@ -426,7 +465,7 @@ __global__ __launch_bounds__(DC_THREADS) void decode_combine_kernel(DecodeParams
 template <int D>
 hipError_t launch_d(const DecodeParams& p, bool need_combine, hipStream_t stream) {
   using Lay = DcLayout<D>;
-  const size_t lds = (Lay::O_FLOATS + 2 * DC_WAVES * 32) * sizeof(float) +
+  const size_t lds = Lay::Q_BYTES + (Lay::O_FLOATS + 2 * DC_WAVES * 32) * sizeof(float) +
                      (DC_WAVES + 4) * sizeof(long long);
   auto kern = decode_split_kernel<D>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -435,10 +474,10 @@ hipError_t launch_d(const DecodeParams& p, bool need_combine, hipStream_t stream
   hipLaunchKernelGGL(kern, dim3(p.n_wg), dim3(DC_THREADS), lds, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess || !need_combine) return e;
-  constexpr int HPB = DC_THREADS / (D / 4);
+  constexpr int HPB = CB_THREADS / (D / 4);
   const int heads = p.g < 32 ? p.g : 32;
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(p.n_units, (heads + HPB - 1) / HPB),
-                     dim3(DC_THREADS), 0, stream, p);
+                     dim3(CB_THREADS), 0, stream, p);
   return hipGetLastError();
 }
 
