@@ -89,10 +89,17 @@ def _run_decode(c):
                workspace=c["ws"], out=c["out"])
 
 
-def _time_loop(fn, c, reps, warm):
+def _time_loop(fn, c, reps, warm, warm_s=1.0):
+    """Mean of `reps` timed calls after `warm` calls and at least warm_s
+    seconds of untimed work (so the clocks are at their sustained level)."""
     import torch
-    for _ in range(warm):
+    t_end = time.perf_counter() + warm_s
+    n = 0
+    while n < warm or time.perf_counter() < t_end:
         fn(c)
+        n += 1
+        if n % 64 == 0:
+            torch.cuda.synchronize()
     evs = _events(reps)
     torch.cuda.synchronize()
     for a, b in evs:
@@ -227,7 +234,9 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=10000,
+                    help="untimed steps before timing; the default (~2 s of work) lets the "
+                         "GPU clocks settle at their sustained level")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the extra workloads")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)

@@ -114,6 +114,10 @@ int gqa_prefill(int dtype, const void* q, const void* k, const void* v, void* o,
   p.nrb = (int)nrb;
   p.n_wg = (int)n_wg;
   p.per_xcd = (int)((n_wg + 7) / 8);
+  // With ragged lengths the bf16 kernel sorts the (b, kvh) units by length and deals
+  // them to the 8 XCD queues in snake order: each queue gets ceil(units / 8) units.
+  p.lpt = (dtype == GQA_DTYPE_BF16 && seqlens && B <= gqa::kPrefillLptMaxB) ? 1 : 0;
+  if (p.lpt) p.per_xcd = (int)(((long long)B * Hkv + 7) / 8 * nrb);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = dtype == GQA_DTYPE_BF16 ? gqa::launch_prefill_bf16(p, causal, s)

@@ -23,8 +23,12 @@ struct PrefillParams {
   int rows_per_wg;    // flattened rows per workgroup
   int nrb;            // row blocks per (b, kvh) unit
   int n_wg;           // B * Hkv * nrb
-  int per_xcd;        // ceil(n_wg / 8)
+  int per_xcd;        // workgroups per XCD queue
+  int lpt;            // 1: deal (b, kvh) units to XCDs longest sequence first (needs seqlens)
 };
+
+// Largest batch for which the bf16 prefill orders its work by sequence length.
+constexpr int kPrefillLptMaxB = 256;
 
 // Decode: workgroups split the concatenated key tiles of all units
 // u = (b, kvh, query block) into equal shares (see decode_bf16.hip).

@@ -133,24 +133,58 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WG_PER_CU) void pr
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  // Launch index -> logical block. Workgroups are dealt round-robin to the 8 XCDs;
-  // giving each XCD a contiguous range of logical blocks keeps the blocks of one
-  // (b, kvh) unit, which share K/V, in the same L2.
-  const int lin = blockIdx.x;
-  const int logical = (lin & 7) * p.per_xcd + (lin >> 3);
-  if (logical >= p.n_wg) return;
-  const int unit = logical / p.nrb;
-  int rb = logical - unit * p.nrb;
-  if (CAUSAL) rb = p.nrb - 1 - rb;  // heaviest row blocks first
-  const int b = unit / p.Hkv;
-  const int kvh = unit - b * p.Hkv;
+  // Launch index -> work. Workgroups are dealt round-robin to the 8 XCDs (launch index
+  // lin runs on XCD lin % 8, in increasing lin / 8); all row blocks of one (b, kvh) unit,
+  // which share K/V, go to the same XCD so the unit's K/V stays in that XCD's L2.
   const int g = p.g, S = p.S, Hq = p.Hq, Hkv = p.Hkv;
-
-  int Lb = S;
-  if (p.seqlens) {
-    Lb = p.seqlens[b];
-    Lb = Lb < 0 ? 0 : (Lb > S ? S : Lb);
+  const int lin = blockIdx.x;
+  const int xcd = lin & 7, qpos = lin >> 3;
+  int b, kvh, rb, Lb = S;
+  if (p.lpt) {
+    // Ragged batch: sort the sequences by length (longest first, ties by index) and deal
+    // the units of that order to the XCD queues in snake order 0..7, 7..0, ..., so every
+    // XCD gets about the same number of key tiles and each queue runs its longest units
+    // first. The lengths are staged in the (not yet used) K/V ring.
+    int* s_len = reinterpret_cast<int*>(smem);
+    int* s_sel = s_len + kPrefillLptMaxB;
+    for (int i = tid; i < p.B; i += Shp::THREADS) {
+      const int L = p.seqlens[i];
+      s_len[i] = L < 0 ? 0 : (L > S ? S : L);
+    }
+    __syncthreads();
+    const int upos = qpos / p.nrb;                          // unit slot in this queue
+    const int r = 8 * upos + ((upos & 1) ? 7 - xcd : xcd);  // rank of the unit
+    if (r >= p.B * Hkv) return;                             // uniform per workgroup
+    const int rank_b = r / Hkv;                             // rank of the sequence
+    kvh = r - rank_b * Hkv;
+    rb = qpos - upos * p.nrb;
+    for (int i = tid; i < p.B; i += Shp::THREADS) {
+      const int Li = s_len[i];
+      int rank = 0;
+      for (int j = 0; j < p.B; ++j) {
+        const int Lj = s_len[j];
+        rank += (Lj > Li) | ((Lj == Li) & (j < i));
+      }
+      if (rank == rank_b) *s_sel = i;
+    }
+    __syncthreads();
+    b = *s_sel;
+    Lb = s_len[b];
+    __syncthreads();  // the ring is written by the first copies below
+  } else {
+    // Each XCD takes a contiguous range of logical blocks.
+    const int logical = xcd * p.per_xcd + qpos;
+    if (logical >= p.n_wg) return;
+    const int unit = logical / p.nrb;
+    rb = logical - unit * p.nrb;
+    b = unit / Hkv;
+    kvh = unit - b * Hkv;
+    if (p.seqlens) {
+      Lb = p.seqlens[b];
+      Lb = Lb < 0 ? 0 : (Lb > S ? S : Lb);
+    }
   }
+  if (CAUSAL) rb = p.nrb - 1 - rb;  // heaviest row blocks first
   const int R = S * g;
   const int f0 = rb * ROWS;
   const int fw = f0 + wave * 32;

@@ -113,6 +113,28 @@ def test_prefill_edge_lengths_and_scales(oracle_mod, dtype):
             assert e <= TOL[dtype] and le <= LSE_TOL[dtype], (e, le)
 
 
+@pytest.mark.parametrize("B,S,Hq,Hkv,d", [(40, 70, 4, 2, 64), (19, 130, 6, 3, 128),
+                                           (300, 20, 2, 1, 32)])
+def test_prefill_many_ragged_sequences(oracle_mod, B, S, Hq, Hkv, d):
+    """Many sequences with repeated, zero and over-long lengths: the bf16 kernel orders its
+    work by sequence length (up to 256 sequences) and must still write every output once."""
+    rng = np.random.default_rng(B + S)
+    lens = rng.integers(0, S + 1, size=B)
+    lens[: B // 4] = lens[B // 4]          # ties
+    lens[-1] = 0
+    lens[-2] = S + 9                       # clamped to S
+    lens = [int(x) for x in lens]
+    q = _rand((B, S, Hq, d), 31, torch.bfloat16)
+    k = _rand((B, S, Hkv, d), 32, torch.bfloat16)
+    v = _rand((B, S, Hkv, d), 33, torch.bfloat16)
+    for causal in (False, True):
+        _say(f"case ragged B={B} S={S} Hq={Hq} Hkv={Hkv} d={d} causal={causal}")
+        e, le = _run_prefill_full(oracle_mod, q, k, v, lens, causal, 1 / math.sqrt(d),
+                                  torch.bfloat16)
+        _say(f"  max_abs_err={e:.3e} lse_err={le:.3e}")
+        assert e <= 2e-2 and le <= 1e-3
+
+
 def test_prefill_poisoned_padding_does_not_leak(oracle_mod):
     """K/V rows at or past a sequence's length hold NaN/Inf: the output must not see them."""
     B, S, Hq, Hkv, d = 3, 150, 8, 2, 128
