@@ -37,7 +37,7 @@ namespace {
 
 constexpr int kRing = 4;      // LDS slots per K and per V ring
 constexpr int kAhead = 3;     // tiles in flight ahead of the one being read
-constexpr float kTau = 8.0f;  // exp2 headroom before the running max is refreshed
+constexpr float kSumCap = 4294967296.0f;  // 2^32: a tile's weights stay at most this large
 
 // Waves per workgroup and workgroups per CU for head size D.
 template <int D>
@@ -309,59 +309,86 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WG_PER_CU) void pr
   };
 
   // ---- online softmax state (one query row per lane; lanes l and l^32 share a row)
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = 0.f, l_run = 0.f;
   const float c = p.scale_log2;
 
-  auto tile = [&](int t) {
-    f32x16 s[NKB];
-    qk(s, kslot(t));
-    const int t0 = t * PF_BN;
-    if (t0 + PF_BN > wave_mask_from) {
-      // Key j = t0 + 32kb + 8(r/4) + 4hh + (r%4) is kept iff j < lim: the sign of j - lim
-      // selects between the score and -inf bit patterns (no compare masks in SGPRs).
-      const int base = t0 + 4 * hh - lim;
+  // Key j = t0 + 32kb + 8(r/4) + 4hh + (r%4) is kept iff j < lim: the sign of j - lim
+  // selects between the score and -inf bit patterns (no compare masks in SGPRs).
+  auto mask = [&](f32x16 (&s)[NKB], int t0) {
+    const int base = t0 + 4 * hh - lim;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const uint32_t keep = (uint32_t)((base + 32 * kb + 8 * (r >> 2) + (r & 3)) >> 31);
-          s[kb][r] = __uint_as_float((__float_as_uint(s[kb][r]) & keep) | (0xff800000u & ~keep));
-        }
-    }
-    float mx = m_run;
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t keep = (uint32_t)((base + 32 * kb + 8 * (r >> 2) + (r & 3)) >> 31);
+        s[kb][r] = __uint_as_float((__float_as_uint(s[kb][r]) & keep) | (0xff800000u & ~keep));
+      }
+  };
+  // Row max over the tile (the other keys of this row sit in lane l ^ 32).
+  auto row_max = [&](const f32x16 (&s)[NKB]) {
+    float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = pair_max(mx);  // the other keys of this row sit in lane l ^ 32
-    const bool fresh = m_run == -INFINITY;
-    const bool refresh = fresh ? (mx != -INFINITY) : ((mx - m_run) * c > kTau);
-    if (wave_any(refresh)) {
-      const float m_new = refresh ? mx : m_run;
-      const float alpha = refresh ? (fresh ? 0.f : fast_exp2((m_run - m_new) * c)) : 1.f;
+    return pair_max(mx);
+  };
+  // Weights exp2(c s - c m) rounded to bf16 as the PV operand; returns this lane's sum of
+  // the rounded weights (the same values the PV product uses). exp2(-inf) = 0.
+  const bf16x2 ones2 = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+  auto weights = [&](const f32x16 (&s)[NKB], bf16x8 (&pp)[NKS]) {
+    const float msc = m_run * c;
+    float lsum = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      u32x4 u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x2 e = {fast_exp2(fmaf(s[ks >> 1][8 * (ks & 1) + 2 * i], c, -msc)),
+                         fast_exp2(fmaf(s[ks >> 1][8 * (ks & 1) + 2 * i + 1], c, -msc))};
+        const bf16x2 h = __builtin_convertvector(e, bf16x2);
+        u[i] = __builtin_bit_cast(uint32_t, h);
+        // The dot operand is the converted pair itself: bit-casting it back out of u[i]
+        // makes this compiler feed the same register to every dot instruction.
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(h, ones2, lsum, false);
+      }
+      pp[ks] = as_bf16x8(u);
+    }
+    return lsum;
+  };
+
+  // The exponent offset m_run is the row max of the first tile and stays fixed while every
+  // weight of a tile is at most 2^kTau (checked through the tile's weight sum, which bounds
+  // each weight). A tile that breaks this (scores grown past the offset) is redone with
+  // the offset raised to its row max, after rescaling what was accumulated. Every term of
+  // a row always shares one offset, so the normalised result is that of the exact max.
+  auto tile = [&](int t) {
+    f32x16 s[NKB];
+    qk(s, kslot(t));
+    const int t0 = t * PF_BN;
+    const bool masked = t0 + PF_BN > wave_mask_from;
+    if (masked) mask(s, t0);
+    if (t == 0) {
+      const float mx = row_max(s);     // key 0 is visible to every row, so mx is finite
+      m_run = mx == -INFINITY ? 0.f : mx;
+    }
+    bf16x8 pp[NKS];
+    float lsum = weights(s, pp);
+    if (wave_any(!(lsum <= kSumCap))) {
+      // Recompute the scores from the K tile (still in LDS) rather than keeping them live
+      // through the common path: the empty asm keeps the compiler from reusing them.
+      asm volatile("" ::: "memory");
+      qk(s, kslot(t));
+      if (masked) mask(s, t0);
+      const float m_new = fmaxf(m_run, row_max(s));
+      const float alpha = fast_exp2((m_run - m_new) * c);
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
       m_run = m_new;
-    }
-    const float msc = (m_run == -INFINITY ? 0.f : m_run) * c;
-    bf16x8 pp[NKS];
-    float lsum = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      float e[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        e[i] = fast_exp2(fmaf(s[ks >> 1][8 * (ks & 1) + i], c, -msc));  // exp2(-inf) = 0
-      u32x4 u;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        u[i] = pack_bf16x2(e[2 * i], e[2 * i + 1]);
-        lsum += e[2 * i] + e[2 * i + 1];
-      }
-      pp[ks] = as_bf16x8(u);
+      lsum = weights(s, pp);
     }
     l_run += lsum;
     pv(pp, vslot(t));

@@ -2,8 +2,12 @@
 
 Tolerances (max |O_gpu - O_oracle| over every checked element):
   fp32 inputs: 1e-5;  bf16 inputs with fp32 accumulation and bf16 output: 2e-2.
-LSE (natural log): 1e-4 for fp32 paths, 1e-3 for bf16 paths (the scores are exact
-products of the stored inputs accumulated in fp32, so LSE sees no bf16 rounding).
+LSE (natural log): 1e-4 for fp32 paths. bf16 decode: 1e-3 (the scores are exact
+products of the stored inputs accumulated in fp32 and the weight sums are fp32).
+bf16 prefill: 2.5e-3. Its weights are rounded to bf16 (relative error <= 2^-9 each)
+for the PV product and the row sum adds those same rounded weights, so the output is
+normalised by exactly the weights it uses, and the sum (of positive terms) is off by
+a relative 2^-9 at most: ln(1 + 2^-9) = 1.95e-3, plus fp32 rounding.
 """
 import math
 import sys
@@ -18,7 +22,8 @@ import workloads as W
 pytestmark = pytest.mark.gpu
 
 TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-2}
-LSE_TOL = {torch.float32: 1e-4, torch.bfloat16: 1e-3}
+LSE_TOL = {torch.float32: 1e-4, torch.bfloat16: 2.5e-3}   # prefill
+BF16_DECODE_LSE_TOL = 1e-3
 
 
 def _say(msg):
@@ -132,7 +137,7 @@ def test_prefill_many_ragged_sequences(oracle_mod, B, S, Hq, Hkv, d):
         e, le = _run_prefill_full(oracle_mod, q, k, v, lens, causal, 1 / math.sqrt(d),
                                   torch.bfloat16)
         _say(f"  max_abs_err={e:.3e} lse_err={le:.3e}")
-        assert e <= 2e-2 and le <= 1e-3
+        assert e <= 2e-2 and le <= LSE_TOL[torch.bfloat16]
 
 
 def test_prefill_poisoned_padding_does_not_leak(oracle_mod):
@@ -149,7 +154,7 @@ def test_prefill_poisoned_padding_does_not_leak(oracle_mod):
     for causal in (False, True):
         e, le = _run_prefill_full(oracle_mod, q, kp, vp, lens, causal, 1 / math.sqrt(d),
                                   torch.bfloat16)
-        assert e <= 2e-2 and le <= 1e-3
+        assert e <= 2e-2 and le <= LSE_TOL[torch.bfloat16]
 
 
 def _sample_rows(B, S, Hq, seqlens, n_random, seed):
@@ -186,7 +191,7 @@ def test_prefill_full_size_sampled(oracle_mod, name):
     e = _max_err(got, ref_o)
     le = _lse_err(got_l, ref_l)
     _say(f"  rows={len(rows)} max_abs_err={e:.3e} lse_err={le:.3e}")
-    assert e <= 2e-2 and le <= 1e-3
+    assert e <= 2e-2 and le <= LSE_TOL[torch.bfloat16]
     assert torch.isfinite(o.float()).all()
 
 
@@ -254,7 +259,7 @@ def test_decode_sweep(oracle_mod, d, Hq, Hkv):
         for splits in (0, 1, 3):
             e, le, _ = _run_decode_full(oracle_mod, q, kc, vc, lens, 1 / math.sqrt(d), splits)
             _say(f"  lens={lens} splits={splits} max_abs_err={e:.3e} lse_err={le:.3e}")
-            assert e <= 2e-2 and le <= 1e-3
+            assert e <= 2e-2 and le <= BF16_DECODE_LSE_TOL
 
 
 def test_decode_poisoned_cache_and_split_invariance(oracle_mod):
@@ -271,7 +276,7 @@ def test_decode_poisoned_cache_and_split_invariance(oracle_mod):
     for splits in (0, 1, 2, 7, 40):
         _say(f"case decode poison splits={splits}")
         e, le, o = _run_decode_full(oracle_mod, q, kc, vc, lens, 0.09, splits)
-        assert e <= 2e-2 and le <= 1e-3
+        assert e <= 2e-2 and le <= BF16_DECODE_LSE_TOL
         outs.append(o.float())
     for o in outs[1:]:
         assert (o - outs[0]).abs().max().item() <= 2e-2
@@ -284,7 +289,7 @@ def test_decode_scales(oracle_mod):
     vc = _rand((B, Hkv, max_len, d), 73, torch.bfloat16)
     for scale in (0.0, -0.3, 0.7):
         e, le, _ = _run_decode_full(oracle_mod, q, kc, vc, [100, 50, 3], scale)
-        assert e <= 2e-2 and le <= 1e-3
+        assert e <= 2e-2 and le <= BF16_DECODE_LSE_TOL
 
 
 def test_decode_equals_last_causal_prefill_row():
@@ -354,7 +359,7 @@ def test_decode_full_size_sampled(oracle_mod, name, use_lens, poison):
     e = _max_err(got, ref_o)
     le = _lse_err(got_l, ref_l)
     _say(f"  pairs={len(pairs)} max_abs_err={e:.3e} lse_err={le:.3e}")
-    assert e <= 2e-2 and le <= 1e-3
+    assert e <= 2e-2 and le <= BF16_DECODE_LSE_TOL
     assert torch.isfinite(o.float()).all()
 
 
