@@ -48,6 +48,7 @@ struct PfShape {
   static constexpr int WG_PER_CU = D == 128 ? 3 : 2;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int ROWS = 32 * WAVES;
+  static constexpr int WAVES_PER_SIMD = WG_PER_CU * WAVES / 4;  // register budget 512 / this
 };
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
@@ -113,7 +114,7 @@ __device__ __forceinline__ void block_barrier() {
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WG_PER_CU) void prefill_bf16_kernel(
+__global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) void prefill_bf16_kernel(
     PrefillParams p) {
   using Lay = PfLayout<D>;
   using Shp = PfShape<D>;
