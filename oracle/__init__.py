@@ -53,10 +53,21 @@ def _load():
                                             dbl, i32, i32, vp, i64, vp, vp, i32]
         lib.oracle_decode.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                       dbl, vp, vp, i32]
+        lib.oracle_prefill_rows_ex.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                               dbl, i32, i32, vp, vp, i64, vp, vp, vp, i32]
+        lib.oracle_prefill_ex.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                          dbl, i32, i32, vp, vp, vp, i32]
+        lib.oracle_decode_pairs_ex.argtypes = [i32, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                               i32, i32, i32, dbl, i32, vp, i32, i32, vp, i64,
+                                               vp, vp, i32]
+        lib.oracle_decode_ex.argtypes = [i32, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                         i32, i32, dbl, i32, vp, vp, vp, i32]
         lib.oracle_mean_pool_heads.argtypes = [i32, vp, i32, i32, i64, vp]
         lib.oracle_max_threads.argtypes = []
         for f in (lib.oracle_prefill_rows, lib.oracle_prefill, lib.oracle_decode_pairs,
-                  lib.oracle_decode, lib.oracle_mean_pool_heads, lib.oracle_max_threads):
+                  lib.oracle_decode, lib.oracle_prefill_rows_ex, lib.oracle_prefill_ex,
+                  lib.oracle_decode_pairs_ex, lib.oracle_decode_ex, lib.oracle_mean_pool_heads,
+                  lib.oracle_max_threads):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -110,8 +121,39 @@ def _lens(lens):
     return np.ascontiguousarray(np.asarray(lens, dtype=np.int32))
 
 
-def prefill(q, k, v, *, scale: float, causal: bool = False, seqlens=None, n_threads: int = 0):
-    """Whole prefill. q [B,S,Hq,d], k/v [B,S,Hkv,d] -> (o [B,S,Hq,d] f64, lse [B,Hq,S] f64)."""
+def _slopes(alibi_slopes, Hq):
+    if alibi_slopes is None:
+        return None
+    try:
+        import torch
+        if isinstance(alibi_slopes, torch.Tensor):
+            alibi_slopes = alibi_slopes.detach().cpu().double().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    a = np.ascontiguousarray(np.asarray(alibi_slopes, dtype=np.float64).reshape(-1))
+    if a.shape != (Hq,):
+        raise ValueError(f"alibi_slopes must have {Hq} entries")
+    return a
+
+
+def _table(block_table):
+    if block_table is None:
+        return None
+    try:
+        import torch
+        if isinstance(block_table, torch.Tensor):
+            block_table = block_table.cpu().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(block_table, dtype=np.int32))
+
+
+def prefill(q, k, v, *, scale: float, causal: bool = False, seqlens=None, window: int = 0,
+            alibi_slopes=None, n_threads: int = 0):
+    """Whole prefill. q [B,S,Hq,d], k/v [B,S,Hkv,d] -> (o [B,S,Hq,d] f64, lse [B,Hq,S] f64).
+
+    window > 0 keeps keys j > i - window; alibi_slopes [Hq] adds -slope_h * |i - j|.
+    """
     qa, qt = _as_host(q)
     ka, kt = _as_host(k)
     va, vt = _as_host(v)
@@ -122,17 +164,20 @@ def prefill(q, k, v, *, scale: float, causal: bool = False, seqlens=None, n_thre
     if ka.shape != (B, S, Hkv, d) or va.shape != ka.shape:
         raise ValueError("shape mismatch")
     sl = _lens(seqlens)
+    sa = _slopes(alibi_slopes, Hq)
     o = np.empty((B, S, Hq, d), np.float64)
     lse = np.empty((B, Hq, S), np.float64)
-    rc = _load().oracle_prefill(qt, _ptr(qa), _ptr(ka), _ptr(va), _ptr(sl), B, S, Hq, Hkv, d,
-                                float(scale), int(bool(causal)), _ptr(o), _ptr(lse), int(n_threads))
+    rc = _load().oracle_prefill_ex(qt, _ptr(qa), _ptr(ka), _ptr(va), _ptr(sl), B, S, Hq, Hkv, d,
+                                   float(scale), int(bool(causal)), int(window), _ptr(sa),
+                                   _ptr(o), _ptr(lse), int(n_threads))
     if rc != 0:
         raise ValueError(f"oracle_prefill rejected the arguments (rc={rc})")
     return o, lse
 
 
 def prefill_rows(q, k, v, rows, *, scale: float, causal: bool = False, seqlens=None,
-                 want_probs: bool = False, n_threads: int = 0):
+                 window: int = 0, alibi_slopes=None, want_probs: bool = False,
+                 n_threads: int = 0):
     """Selected rows. rows: int array [n, 3] of (b, h, i). Returns o [n,d], lse [n] (, p [n,S])."""
     qa, qt = _as_host(q)
     ka, _ = _as_host(k)
@@ -145,48 +190,68 @@ def prefill_rows(q, k, v, rows, *, scale: float, causal: bool = False, seqlens=N
     lse = np.empty((n,), np.float64)
     p = np.empty((n, S), np.float64) if want_probs else None
     sl = _lens(seqlens)
-    rc = _load().oracle_prefill_rows(qt, _ptr(qa), _ptr(ka), _ptr(va), _ptr(sl), B, S, Hq, Hkv,
-                                     d, float(scale), int(bool(causal)), _ptr(r), n, _ptr(o),
-                                     _ptr(lse), _ptr(p), int(n_threads))
+    sa = _slopes(alibi_slopes, Hq)
+    rc = _load().oracle_prefill_rows_ex(qt, _ptr(qa), _ptr(ka), _ptr(va), _ptr(sl), B, S, Hq,
+                                        Hkv, d, float(scale), int(bool(causal)), int(window),
+                                        _ptr(sa), _ptr(r), n, _ptr(o), _ptr(lse), _ptr(p),
+                                        int(n_threads))
     if rc != 0:
         raise ValueError(f"oracle_prefill_rows rejected the arguments (rc={rc})")
     return (o, lse, p) if want_probs else (o, lse)
 
 
-def decode(q, k_cache, v_cache, *, scale: float, lens=None, n_threads: int = 0):
-    """Whole decode. q [B,Hq,d], caches [B,Hkv,max_len,d] -> (o [B,Hq,d], lse [B,Hq])."""
+def _decode_shapes(qa, ka, block_table, page_size):
+    B, Hq, d = qa.shape
+    Hkv = ka.shape[1]
+    bt = _table(block_table)
+    if bt is None:
+        return B, Hq, d, Hkv, ka.shape[2], None, 0, 0, 0
+    if ka.shape[2] != page_size or bt.ndim != 2 or bt.shape[0] != B:
+        raise ValueError("paged cache: pools [num_pages, Hkv, page_size, d], table [B, blocks]")
+    return B, Hq, d, Hkv, bt.shape[1] * page_size, bt, page_size, bt.shape[1], ka.shape[0]
+
+
+def decode(q, k_cache, v_cache, *, scale: float, lens=None, window: int = 0, alibi_slopes=None,
+           block_table=None, page_size: int = 0, n_threads: int = 0):
+    """Whole decode. q [B,Hq,d], caches [B,Hkv,max_len,d] -> (o [B,Hq,d], lse [B,Hq]).
+
+    With block_table [B, blocks] the caches are page pools [num_pages, Hkv, page_size, d].
+    """
     qa, qt = _as_host(q)
     ka, _ = _as_host(k_cache)
     va, _ = _as_host(v_cache)
-    B, Hq, d = qa.shape
-    Hkv, max_len = ka.shape[1], ka.shape[2]
+    B, Hq, d, Hkv, max_len, bt, P, MB, NP = _decode_shapes(qa, ka, block_table, page_size)
     sl = _lens(lens)
+    sa = _slopes(alibi_slopes, Hq)
     o = np.empty((B, Hq, d), np.float64)
     lse = np.empty((B, Hq), np.float64)
-    rc = _load().oracle_decode(qt, _ptr(qa), _ptr(ka), _ptr(va), _ptr(sl), B, Hq, Hkv, d,
-                               max_len, float(scale), _ptr(o), _ptr(lse), int(n_threads))
+    rc = _load().oracle_decode_ex(qt, _ptr(qa), _ptr(ka), _ptr(va), _ptr(sl), _ptr(bt), P, MB, NP,
+                                  B, Hq, Hkv, d, max_len, float(scale), int(window), _ptr(sa),
+                                  _ptr(o), _ptr(lse), int(n_threads))
     if rc != 0:
         raise ValueError(f"oracle_decode rejected the arguments (rc={rc})")
     return o, lse
 
 
 def decode_pairs(q, k_cache, v_cache, pairs, *, scale: float, lens=None, key_range=None,
+                 window: int = 0, alibi_slopes=None, block_table=None, page_size: int = 0,
                  n_threads: int = 0):
     """Selected (b, h) pairs, optionally restricted to keys in [lo, hi)."""
     qa, qt = _as_host(q)
     ka, _ = _as_host(k_cache)
     va, _ = _as_host(v_cache)
-    B, Hq, d = qa.shape
-    Hkv, max_len = ka.shape[1], ka.shape[2]
+    B, Hq, d, Hkv, max_len, bt, P, MB, NP = _decode_shapes(qa, ka, block_table, page_size)
     lo, hi = (0, max_len) if key_range is None else key_range
     pr = np.ascontiguousarray(np.asarray(pairs, dtype=np.int64).reshape(-1, 2))
     n = pr.shape[0]
     o = np.empty((n, d), np.float64)
     lse = np.empty((n,), np.float64)
     sl = _lens(lens)
-    rc = _load().oracle_decode_pairs(qt, _ptr(qa), _ptr(ka), _ptr(va), _ptr(sl), B, Hq, Hkv, d,
-                                     max_len, float(scale), int(lo), int(hi), _ptr(pr), n,
-                                     _ptr(o), _ptr(lse), int(n_threads))
+    sa = _slopes(alibi_slopes, Hq)
+    rc = _load().oracle_decode_pairs_ex(qt, _ptr(qa), _ptr(ka), _ptr(va), _ptr(sl), _ptr(bt), P,
+                                        MB, NP, B, Hq, Hkv, d, max_len, float(scale),
+                                        int(window), _ptr(sa), int(lo), int(hi), _ptr(pr), n,
+                                        _ptr(o), _ptr(lse), int(n_threads))
     if rc != 0:
         raise ValueError(f"oracle_decode_pairs rejected the arguments (rc={rc})")
     return o, lse

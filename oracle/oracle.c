@@ -31,7 +31,19 @@
  *   - padding: seqlens[b] masks KEYS j >= L_b; every query row is computed;
  *   - an empty valid-key set gives O = 0 and LSE = -inf;
  *   - causal means key j is visible to query i iff j <= i (self-attention);
- *   - the decode query sees every cached key j < L_b.
+ *   - the decode query sees every cached key j < L_b and sits at position L_b - 1;
+ *   - sliding window w > 0: key j is also required to satisfy j > i - w (the
+ *     window of Mistral-style models, which the azimuth.plus GQA digest's
+ *     timeline pairs with GQA, "2023: Mistral 7B"; the window is given in keys,
+ *     the query's own key included);
+ *   - ALiBi: the pages' attention signature has an `alibi_slopes` argument
+ *     (gitcode page, section "GQA的分组共享机制") but no formula; the reading
+ *     used is the usual one, score(i, j) = scale * <q_i, k_j> - slope_h * |i - j|,
+ *     the bias added after scaling and before the softmax;
+ *   - paged KV cache (the azimuth.plus digest, "the bigger picture": GQA is
+ *     orthogonal to paged attention and composes with it): K/V rows live in a
+ *     pool of pages [num_pages, H_kv, page_size, d]; key j of sequence b is row
+ *     j % page_size of page block_table[b][j / page_size].
  *
  * Pins (tests/test_oracle_pins.py) tie this file to things other than itself:
  * torch's fp64 scaled_dot_product_attention, closed forms (uniform scores give
@@ -61,19 +73,20 @@ static double ld(const void *p, int dtype, size_t idx) {
 
 /*
  * One attention row, written out as the definition:
- *   for every key j in the valid set:  s_j = scale * <q, k_j>
+ *   for every key j in the valid set:  s_j = scale * <q, k_j> + bias_j
  *   m = max_j s_j,  p_j = exp(s_j - m),  l = sum_j p_j,  P_j = p_j / l
  *   o = sum_j P_j v_j,  lse = m + ln l
  * valid[j] != 0 marks the valid keys among n_keys. K row j starts at element
  * k_off + j * kv_row_stride (likewise V). q starts at q_off. p_out (n_keys
  * entries, may be NULL) receives the explicit probability row (0 for masked
- * keys). Returns the number of valid keys.
+ * keys). bias (n_keys entries) is the additive ALiBi term, or NULL for none.
+ * Returns the number of valid keys.
  */
 static int attend_row(const void *q, int qt, size_t q_off,
                       const void *k, const void *v, int kvt,
                       size_t k_off, size_t v_off, size_t kv_row_stride,
-                      const unsigned char *valid, int n_keys, int d, double scale,
-                      double *s /* scratch [n_keys] */,
+                      const unsigned char *valid, const double *bias, int n_keys, int d,
+                      double scale, double *s /* scratch [n_keys] */,
                       double *o, double *lse, double *p_out) {
     int n_valid = 0;
     double m = -INFINITY;
@@ -82,7 +95,7 @@ static int attend_row(const void *q, int qt, size_t q_off,
         double dot = 0.0;
         for (int t = 0; t < d; ++t)
             dot += ld(q, qt, q_off + t) * ld(k, kvt, k_off + (size_t)j * kv_row_stride + t);
-        s[j] = scale * dot;
+        s[j] = scale * dot + (bias ? bias[j] : 0.0);
         if (s[j] > m) m = s[j];
         ++n_valid;
     }
@@ -129,11 +142,12 @@ static int clamp_len(const int32_t *lens, int b, int cap) {
  *   o:       [n_rows, d]   lse: [n_rows]   p_rows (optional): [n_rows, S]
  * Returns 0, or -1 on invalid shapes.
  */
-int oracle_prefill_rows(int dtype, const void *q, const void *k, const void *v,
-                        const int32_t *seqlens, int B, int S, int Hq, int Hkv, int d,
-                        double scale, int causal, const int64_t *rows, int64_t n_rows,
-                        double *o, double *lse, double *p_rows, int n_threads) {
-    if (B <= 0 || S <= 0 || d <= 0 || !check_heads(Hq, Hkv)) return -1;
+int oracle_prefill_rows_ex(int dtype, const void *q, const void *k, const void *v,
+                           const int32_t *seqlens, int B, int S, int Hq, int Hkv, int d,
+                           double scale, int causal, int window, const double *alibi_slopes,
+                           const int64_t *rows, int64_t n_rows,
+                           double *o, double *lse, double *p_rows, int n_threads) {
+    if (B <= 0 || S <= 0 || d <= 0 || !check_heads(Hq, Hkv) || window < 0) return -1;
     const int g = Hq / Hkv;
 #ifdef _OPENMP
     if (n_threads > 0) omp_set_num_threads(n_threads);
@@ -144,6 +158,7 @@ int oracle_prefill_rows(int dtype, const void *q, const void *k, const void *v,
 #pragma omp parallel
     {
         double *s = (double *)malloc(sizeof(double) * (size_t)S);
+        double *bias = alibi_slopes ? (double *)malloc(sizeof(double) * (size_t)S) : NULL;
         unsigned char *valid = (unsigned char *)malloc((size_t)S);
 #pragma omp for schedule(dynamic, 4)
         for (int64_t r = 0; r < n_rows; ++r) {
@@ -151,26 +166,39 @@ int oracle_prefill_rows(int dtype, const void *q, const void *k, const void *v,
             if (b < 0 || b >= B || h < 0 || h >= Hq || i < 0 || i >= S) { bad = 1; continue; }
             const int kvh = h / g; /* contiguous grouping */
             const int L = clamp_len(seqlens, b, S);
-            for (int j = 0; j < S; ++j)
-                valid[j] = (unsigned char)(j < L && (!causal || j <= i));
+            for (int j = 0; j < S; ++j) {
+                valid[j] = (unsigned char)(j < L && (!causal || j <= i) &&
+                                           (window == 0 || j > i - window));
+                if (bias) bias[j] = -alibi_slopes[h] * fabs((double)(i - j));
+            }
             const size_t q_off = (((size_t)b * S + i) * Hq + h) * (size_t)d;
             const size_t kv_off = ((size_t)b * S * Hkv + kvh) * (size_t)d;
             attend_row(q, dtype, q_off, k, v, dtype, kv_off, kv_off, (size_t)Hkv * d,
-                       valid, S, d, scale, s, o + (size_t)r * d, lse + r,
+                       valid, bias, S, d, scale, s, o + (size_t)r * d, lse + r,
                        p_rows ? p_rows + (size_t)r * S : NULL);
         }
         free(s);
+        free(bias);
         free(valid);
     }
     return bad ? -1 : 0;
 }
 
+int oracle_prefill_rows(int dtype, const void *q, const void *k, const void *v,
+                        const int32_t *seqlens, int B, int S, int Hq, int Hkv, int d,
+                        double scale, int causal, const int64_t *rows, int64_t n_rows,
+                        double *o, double *lse, double *p_rows, int n_threads) {
+    return oracle_prefill_rows_ex(dtype, q, k, v, seqlens, B, S, Hq, Hkv, d, scale, causal, 0,
+                                  NULL, rows, n_rows, o, lse, p_rows, n_threads);
+}
+
 /*
  * Full prefill: o [B, S, Hq, d] (same layout as q), lse [B, Hq, S].
  */
-int oracle_prefill(int dtype, const void *q, const void *k, const void *v,
-                   const int32_t *seqlens, int B, int S, int Hq, int Hkv, int d,
-                   double scale, int causal, double *o, double *lse, int n_threads) {
+int oracle_prefill_ex(int dtype, const void *q, const void *k, const void *v,
+                      const int32_t *seqlens, int B, int S, int Hq, int Hkv, int d,
+                      double scale, int causal, int window, const double *alibi_slopes,
+                      double *o, double *lse, int n_threads) {
     if (B <= 0 || S <= 0 || d <= 0 || !check_heads(Hq, Hkv)) return -1;
     const int64_t n = (int64_t)B * S * Hq;
     int64_t *rows = (int64_t *)malloc(sizeof(int64_t) * 3 * (size_t)n);
@@ -183,8 +211,9 @@ int oracle_prefill(int dtype, const void *q, const void *k, const void *v,
             for (int h = 0; h < Hq; ++h, ++r) {
                 rows[3 * r] = b; rows[3 * r + 1] = h; rows[3 * r + 2] = i;
             }
-    int rc = oracle_prefill_rows(dtype, q, k, v, seqlens, B, S, Hq, Hkv, d, scale, causal,
-                                 rows, n, o_rows, l_rows, NULL, n_threads);
+    int rc = oracle_prefill_rows_ex(dtype, q, k, v, seqlens, B, S, Hq, Hkv, d, scale, causal,
+                                    window, alibi_slopes, rows, n, o_rows, l_rows, NULL,
+                                    n_threads);
     if (rc == 0) {
         /* rows were enumerated in [B, S, Hq] order, matching o's layout */
         memcpy(o, o_rows, sizeof(double) * (size_t)n * d);
@@ -198,21 +227,37 @@ int oracle_prefill(int dtype, const void *q, const void *k, const void *v,
     return rc;
 }
 
+int oracle_prefill(int dtype, const void *q, const void *k, const void *v,
+                   const int32_t *seqlens, int B, int S, int Hq, int Hkv, int d,
+                   double scale, int causal, double *o, double *lse, int n_threads) {
+    return oracle_prefill_ex(dtype, q, k, v, seqlens, B, S, Hq, Hkv, d, scale, causal, 0, NULL,
+                             o, lse, n_threads);
+}
+
 /*
  * Decode for an explicit list of (b, h) pairs: one query token per sequence
  * over a KV cache.
- *   q: [B, Hq, d]   k_cache, v_cache: [B, Hkv, max_len, d]   lens: [B] or NULL
- *   pairs: n_pairs (b, h) pairs;  o: [n_pairs, d];  lse: [n_pairs]
- *   key range: keys j in [j_lo, min(L_b, j_hi)) are the valid set (j_lo = 0,
- *   j_hi = max_len gives the whole cache; a sub-range is used only to check the
- *   split identity).
+ *   q: [B, Hq, d];  lens: [B] or NULL;  pairs: n_pairs (b, h);  o: [n_pairs, d];
+ *   lse: [n_pairs].
+ *   Contiguous cache (block_table == NULL): k_cache, v_cache [B, Hkv, max_len, d].
+ *   Paged cache: k_cache, v_cache are page pools [num_pages, Hkv, page_size, d],
+ *   block_table [B, max_blocks] page ids, max_len = max_blocks * page_size; the
+ *   valid keys of each sequence are first gathered into a contiguous buffer.
+ *   The query sits at position L_b - 1: window > 0 keeps keys j > L_b - 1 - window,
+ *   ALiBi adds -slope_h * (L_b - 1 - j).
+ *   key range: keys j in [j_lo, j_hi) are also required (j_lo = 0, j_hi = max_len
+ *   is the whole cache; a sub-range is used only to check the split identity).
  */
-int oracle_decode_pairs(int dtype, const void *q, const void *k_cache, const void *v_cache,
-                        const int32_t *lens, int B, int Hq, int Hkv, int d, int max_len,
-                        double scale, int j_lo, int j_hi,
-                        const int64_t *pairs, int64_t n_pairs,
-                        double *o, double *lse, int n_threads) {
-    if (B <= 0 || max_len <= 0 || d <= 0 || !check_heads(Hq, Hkv)) return -1;
+int oracle_decode_pairs_ex(int dtype, const void *q, const void *k_cache, const void *v_cache,
+                           const int32_t *lens, const int32_t *block_table, int page_size,
+                           int max_blocks, int num_pages, int B, int Hq, int Hkv, int d,
+                           int max_len, double scale, int window, const double *alibi_slopes,
+                           int j_lo, int j_hi, const int64_t *pairs, int64_t n_pairs,
+                           double *o, double *lse, int n_threads) {
+    if (B <= 0 || max_len <= 0 || d <= 0 || !check_heads(Hq, Hkv) || window < 0) return -1;
+    if (block_table && (page_size <= 0 || max_blocks <= 0 || num_pages <= 0 ||
+                        (int64_t)page_size * max_blocks != max_len))
+        return -1;
     const int g = Hq / Hkv;
 #ifdef _OPENMP
     if (n_threads > 0) omp_set_num_threads(n_threads);
@@ -223,39 +268,87 @@ int oracle_decode_pairs(int dtype, const void *q, const void *k_cache, const voi
 #pragma omp parallel
     {
         double *s = (double *)malloc(sizeof(double) * (size_t)max_len);
+        double *bias = alibi_slopes ? (double *)malloc(sizeof(double) * (size_t)max_len) : NULL;
         unsigned char *valid = (unsigned char *)malloc((size_t)max_len);
+        double *kg = NULL, *vg = NULL;
+        if (block_table) {
+            kg = (double *)malloc(sizeof(double) * (size_t)max_len * d);
+            vg = (double *)malloc(sizeof(double) * (size_t)max_len * d);
+        }
 #pragma omp for schedule(dynamic, 1)
         for (int64_t r = 0; r < n_pairs; ++r) {
             const int b = (int)pairs[2 * r], h = (int)pairs[2 * r + 1];
             if (b < 0 || b >= B || h < 0 || h >= Hq) { bad = 1; continue; }
             const int kvh = h / g;
             const int L = clamp_len(lens, b, max_len);
-            for (int j = 0; j < max_len; ++j)
-                valid[j] = (unsigned char)(j < L && j >= j_lo && j < j_hi);
+            const int qpos = L - 1;
+            for (int j = 0; j < max_len; ++j) {
+                valid[j] = (unsigned char)(j < L && j >= j_lo && j < j_hi &&
+                                           (window == 0 || j > qpos - window));
+                if (bias) bias[j] = -alibi_slopes[h] * fabs((double)(qpos - j));
+            }
             const size_t q_off = ((size_t)b * Hq + h) * (size_t)d;
-            const size_t kv_off = ((size_t)b * Hkv + kvh) * (size_t)max_len * d;
-            attend_row(q, dtype, q_off, k_cache, v_cache, dtype, kv_off, kv_off, (size_t)d,
-                       valid, max_len, d, scale, s, o + (size_t)r * d, lse + r, NULL);
+            if (!block_table) {
+                const size_t kv_off = ((size_t)b * Hkv + kvh) * (size_t)max_len * d;
+                attend_row(q, dtype, q_off, k_cache, v_cache, dtype, kv_off, kv_off, (size_t)d,
+                           valid, bias, max_len, d, scale, s, o + (size_t)r * d, lse + r, NULL);
+                continue;
+            }
+            /* gather: key j of sequence b is row j % page_size of page table[b][j / page_size] */
+            for (int j = 0; j < L; ++j) {
+                const int page = block_table[(size_t)b * max_blocks + j / page_size];
+                if (page < 0 || page >= num_pages) { bad = 1; break; }
+                const size_t src = (((size_t)page * Hkv + kvh) * page_size + j % page_size) * d;
+                for (int t = 0; t < d; ++t) {
+                    kg[(size_t)j * d + t] = ld(k_cache, dtype, src + t);
+                    vg[(size_t)j * d + t] = ld(v_cache, dtype, src + t);
+                }
+            }
+            attend_row(q, dtype, q_off, kg, vg, ORC_F64, 0, 0, (size_t)d, valid, bias, max_len,
+                       d, scale, s, o + (size_t)r * d, lse + r, NULL);
         }
         free(s);
+        free(bias);
         free(valid);
+        free(kg);
+        free(vg);
     }
     return bad ? -1 : 0;
 }
 
+int oracle_decode_pairs(int dtype, const void *q, const void *k_cache, const void *v_cache,
+                        const int32_t *lens, int B, int Hq, int Hkv, int d, int max_len,
+                        double scale, int j_lo, int j_hi,
+                        const int64_t *pairs, int64_t n_pairs,
+                        double *o, double *lse, int n_threads) {
+    return oracle_decode_pairs_ex(dtype, q, k_cache, v_cache, lens, NULL, 0, 0, 0, B, Hq, Hkv, d,
+                                  max_len, scale, 0, NULL, j_lo, j_hi, pairs, n_pairs, o, lse,
+                                  n_threads);
+}
+
 /* Full decode: o [B, Hq, d], lse [B, Hq]. */
-int oracle_decode(int dtype, const void *q, const void *k_cache, const void *v_cache,
-                  const int32_t *lens, int B, int Hq, int Hkv, int d, int max_len,
-                  double scale, double *o, double *lse, int n_threads) {
+int oracle_decode_ex(int dtype, const void *q, const void *k_cache, const void *v_cache,
+                     const int32_t *lens, const int32_t *block_table, int page_size,
+                     int max_blocks, int num_pages, int B, int Hq, int Hkv, int d, int max_len,
+                     double scale, int window, const double *alibi_slopes, double *o,
+                     double *lse, int n_threads) {
     if (B <= 0 || Hq <= 0) return -1;
     const int64_t n = (int64_t)B * Hq;
     int64_t *pairs = (int64_t *)malloc(sizeof(int64_t) * 2 * (size_t)n);
     if (!pairs) return -2;
     for (int64_t r = 0; r < n; ++r) { pairs[2 * r] = r / Hq; pairs[2 * r + 1] = r % Hq; }
-    int rc = oracle_decode_pairs(dtype, q, k_cache, v_cache, lens, B, Hq, Hkv, d, max_len,
-                                 scale, 0, max_len, pairs, n, o, lse, n_threads);
+    int rc = oracle_decode_pairs_ex(dtype, q, k_cache, v_cache, lens, block_table, page_size,
+                                    max_blocks, num_pages, B, Hq, Hkv, d, max_len, scale, window,
+                                    alibi_slopes, 0, max_len, pairs, n, o, lse, n_threads);
     free(pairs);
     return rc;
+}
+
+int oracle_decode(int dtype, const void *q, const void *k_cache, const void *v_cache,
+                  const int32_t *lens, int B, int Hq, int Hkv, int d, int max_len,
+                  double scale, double *o, double *lse, int n_threads) {
+    return oracle_decode_ex(dtype, q, k_cache, v_cache, lens, NULL, 0, 0, 0, B, Hq, Hkv, d,
+                            max_len, scale, 0, NULL, o, lse, n_threads);
 }
 
 /*
