@@ -66,18 +66,34 @@ def _lens_arg(x, B, device, name):
     return x, x.data_ptr()
 
 
+def _slopes_arg(x, Hq, device):
+    """ALiBi slopes as a contiguous fp32 [Hq] device tensor (or None)."""
+    torch = _torch()
+    if x is None:
+        return None, 0
+    if not isinstance(x, torch.Tensor):
+        x = torch.as_tensor(x, dtype=torch.float32)
+    x = x.to(device=device, dtype=torch.float32).contiguous()
+    if x.shape != (Hq,):
+        raise ValueError(f"alibi_slopes must have shape ({Hq},)")
+    return x, x.data_ptr()
+
+
 def _stream_ptr(device) -> int:
     torch = _torch()
     return torch.cuda.current_stream(device).cuda_stream
 
 
 def prefill(q, k, v, *, causal: bool = False, softmax_scale: Optional[float] = None,
-            seqlens=None, return_lse: bool = False, out=None, lse_out=None):
+            seqlens=None, window: int = 0, alibi_slopes=None, return_lse: bool = False,
+            out=None, lse_out=None):
     """Attention of every query row over the valid keys of its sequence.
 
     q [B, S, Hq, d], k/v [B, S, Hkv, d] (contiguous, same dtype: bfloat16 or float32,
-    on the GPU), seqlens int32 [B] valid key lengths or None. Returns o [B, S, Hq, d]
-    (and lse [B, Hq, S] float32 when return_lse).
+    on the GPU), seqlens int32 [B] valid key lengths or None. window > 0 (causal
+    only) keeps keys j > i - window; alibi_slopes [Hq] subtracts slope_h * |i - j|
+    from the scaled scores. Returns o [B, S, Hq, d] (and lse [B, Hq, S] float32 when
+    return_lse).
     """
     torch = _torch()
     _check(q, "q", 4)
@@ -102,11 +118,13 @@ def prefill(q, k, v, *, causal: bool = False, softmax_scale: Optional[float] = N
             _check(lse_out, "lse_out", 3, torch.float32)
         lse_ptr = lse_out.data_ptr()
     lens, lens_ptr = _lens_arg(seqlens, B, q.device, "seqlens")
-    st = load().gqa_prefill(_dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                            out.data_ptr(), lse_ptr or None, lens_ptr or None, B, S, Hq, Hkv, d,
-                            scale, int(bool(causal)), _stream_ptr(q.device))
+    slopes, slopes_ptr = _slopes_arg(alibi_slopes, Hq, q.device)
+    st = load().gqa_prefill_ex(_dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                               out.data_ptr(), lse_ptr or None, lens_ptr or None, B, S, Hq, Hkv,
+                               d, scale, int(bool(causal)), int(window), slopes_ptr or None,
+                               _stream_ptr(q.device))
     if st != GQA_OK:
-        raise GQAError(st, "gqa_prefill")
+        raise GQAError(st, "gqa_prefill_ex")
     return (out, lse_out) if return_lse else out
 
 
@@ -120,23 +138,40 @@ def decode_num_workgroups(B: int, Hq: int, Hkv: int, max_len: int, num_splits: i
 
 
 def decode(q, k_cache, v_cache, cache_lens=None, *, softmax_scale: Optional[float] = None,
-           num_splits: int = 0, return_lse: bool = False, workspace=None, out=None,
+           num_splits: int = 0, window: int = 0, alibi_slopes=None, block_table=None,
+           page_size: int = 0, return_lse: bool = False, workspace=None, out=None,
            lse_out=None):
     """One query token per sequence over its KV cache.
 
     q [B, Hq, d], k_cache/v_cache [B, Hkv, max_len, d] (bfloat16, contiguous, on the
-    GPU), cache_lens int32 [B] or None (= max_len). Returns o [B, Hq, d] (and lse
-    [B, Hq] float32 when return_lse). `workspace` (uint8 GPU tensor) is allocated
-    when not given.
+    GPU), cache_lens int32 [B] or None (= max_len). With block_table (int32
+    [B, max_blocks]) the caches are page pools [num_pages, Hkv, page_size, d] and
+    key j of sequence b is row j % page_size of page block_table[b, j // page_size].
+    window > 0 keeps only each sequence's last `window` keys; alibi_slopes [Hq]
+    subtracts slope_h * (L_b - 1 - j). Returns o [B, Hq, d] (and lse [B, Hq] float32
+    when return_lse). `workspace` (uint8 GPU tensor) is allocated when not given.
     """
     torch = _torch()
     _check(q, "q", 3)
     _check(k_cache, "k_cache", 4, q.dtype)
     _check(v_cache, "v_cache", 4, q.dtype)
     B, Hq, d = q.shape
-    Hkv, max_len = k_cache.shape[1], k_cache.shape[2]
-    if tuple(k_cache.shape) != (B, Hkv, max_len, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
-        raise ValueError("k_cache and v_cache must be [B, Hkv, max_len, d]")
+    Hkv = k_cache.shape[1]
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or k_cache.shape[3] != d:
+        raise ValueError("k_cache and v_cache must have the same shape, last dim d")
+    table, table_ptr, max_blocks, num_pages = None, 0, 0, 0
+    if block_table is None:
+        max_len = k_cache.shape[2]
+        if k_cache.shape[0] != B:
+            raise ValueError("k_cache and v_cache must be [B, Hkv, max_len, d]")
+    else:
+        _check(block_table, "block_table", 2, torch.int32)
+        if block_table.shape[0] != B or k_cache.shape[2] != page_size:
+            raise ValueError("paged cache: pools [num_pages, Hkv, page_size, d], "
+                             "block_table [B, max_blocks]")
+        table, table_ptr = block_table, block_table.data_ptr()
+        max_blocks, num_pages = block_table.shape[1], k_cache.shape[0]
+        max_len = max_blocks * page_size
     if Hkv <= 0 or Hq % Hkv != 0:
         raise ValueError(f"num_heads_q ({Hq}) must be divisible by num_heads_kv ({Hkv})")
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
@@ -153,10 +188,14 @@ def decode(q, k_cache, v_cache, cache_lens=None, *, softmax_scale: Optional[floa
             lse_out = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
         lse_ptr = lse_out.data_ptr()
     lens, lens_ptr = _lens_arg(cache_lens, B, q.device, "cache_lens")
-    st = load().gqa_decode(_dtype_code(q), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                           lens_ptr or None, out.data_ptr(), lse_ptr or None, B, Hq, Hkv, d,
-                           max_len, scale, int(num_splits), workspace.data_ptr(),
-                           workspace.numel() * workspace.element_size(), _stream_ptr(q.device))
+    slopes, slopes_ptr = _slopes_arg(alibi_slopes, Hq, q.device)
+    st = load().gqa_decode_ex(_dtype_code(q), q.data_ptr(), k_cache.data_ptr(),
+                              v_cache.data_ptr(), lens_ptr or None, table_ptr or None,
+                              int(page_size) if table is not None else 0, max_blocks, num_pages,
+                              out.data_ptr(), lse_ptr or None, B, Hq, Hkv, d, max_len, scale,
+                              int(window), slopes_ptr or None, int(num_splits),
+                              workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                              _stream_ptr(q.device))
     if st != GQA_OK:
-        raise GQAError(st, "gqa_decode")
+        raise GQAError(st, "gqa_decode_ex")
     return (out, lse_out) if return_lse else out

@@ -58,6 +58,12 @@ def load():
     lib.gqa_decode.argtypes = [i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
                                vp, sz, vp]
     lib.gqa_decode.restype = i32
+    lib.gqa_prefill_ex.argtypes = [i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
+                                   i32, i32, vp, vp]
+    lib.gqa_prefill_ex.restype = i32
+    lib.gqa_decode_ex.argtypes = [i32, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, i32, i32, i32,
+                                  i32, i32, f32, i32, vp, i32, vp, sz, vp]
+    lib.gqa_decode_ex.restype = i32
     _lib = lib
     return lib
 

@@ -43,7 +43,14 @@ __device__ __forceinline__ int clamp_len(const int32_t* lens, int b, int cap) {
   return L < 0 ? 0 : (L > cap ? cap : L);
 }
 
-__device__ __forceinline__ int tiles_of(int L) { return (L + DC_TILE - 1) / DC_TILE; }
+// A sequence's key tiles: with a sliding window only the last `window` keys are visited,
+// from tile first_tile(L) on.
+__device__ __forceinline__ int first_tile(int L, int window) {
+  return window > 0 ? max(0, L - window) / DC_TILE : 0;
+}
+__device__ __forceinline__ int tiles_of(int L, int window) {
+  return L > 0 ? (L + DC_TILE - 1) / DC_TILE - first_tile(L, window) : 0;
+}
 
 // Sum over a workgroup of NT threads (all threads get the result).
 template <int NT>
@@ -62,12 +69,12 @@ __device__ long long block_sum(long long v, long long* scratch) {
 
 // Tiles of sequences [0, B) (per K/V unit of one sequence) and of [0, b_end).
 template <int NT>
-__device__ void tile_prefix(const int32_t* lens, int B, int cap, int b_end, long long* total,
-                            long long* before, long long* scratch) {
+__device__ void tile_prefix(const int32_t* lens, int B, int cap, int window, int b_end,
+                            long long* total, long long* before, long long* scratch) {
   long long tot = 0, bef = 0;
   for (int base = 0; base < B; base += NT) {
     const int bb = base + threadIdx.x;
-    const long long tb = bb < B ? tiles_of(clamp_len(lens, bb, cap)) : 0;
+    const long long tb = bb < B ? tiles_of(clamp_len(lens, bb, cap), window) : 0;
     tot += block_sum<NT>(tb, scratch);
     bef += block_sum<NT>(bb < b_end ? tb : 0, scratch);
   }
@@ -77,8 +84,8 @@ __device__ void tile_prefix(const int32_t* lens, int B, int cap, int b_end, long
 
 // First sequence whose tile range (in concatenated unit order) ends after tile t0,
 // and the first tile of that sequence.
-__device__ void find_seq(const int32_t* lens, int B, int cap, long long HU, long long t0,
-                         int* b_out, long long* start_out, long long* scratch) {
+__device__ void find_seq(const int32_t* lens, int B, int cap, int window, long long HU,
+                         long long t0, int* b_out, long long* start_out, long long* scratch) {
   long long run = 0;  // tiles of sequences before this chunk
   if (threadIdx.x == 0) {
     scratch[DC_WAVES] = 0;
@@ -86,7 +93,7 @@ __device__ void find_seq(const int32_t* lens, int B, int cap, long long HU, long
   }
   for (int base = 0; base < B; base += DC_THREADS) {
     const int bb = base + threadIdx.x;
-    const long long tb = bb < B ? HU * tiles_of(clamp_len(lens, bb, cap)) : 0;
+    const long long tb = bb < B ? HU * tiles_of(clamp_len(lens, bb, cap), window) : 0;
     // inclusive scan of tb across the workgroup
     long long x = tb;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -128,7 +135,7 @@ struct DcLayout {
   static constexpr int Q_BYTES = 32 * QSTR * 2;
 };
 
-template <int D>
+template <int D, bool ALIBI, bool PAGED>
 __global__ __launch_bounds__(DC_THREADS, 2) void decode_split_kernel(DecodeParams p) {
   constexpr int DPL = D / 32;  // output columns per lane in the V^T operand
   using Lay = DcLayout<D>;
@@ -140,7 +147,7 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_split_kernel(DecodeParam
   long long* scratch = reinterpret_cast<long long*>(s_l + DC_WAVES * 32);  // 8 entries
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
@@ -150,7 +157,7 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_split_kernel(DecodeParam
   const float c = p.scale_log2;
 
   long long T, unused;
-  tile_prefix<DC_THREADS>(p.lens, p.B, cap, 0, &T, &unused, scratch);
+  tile_prefix<DC_THREADS>(p.lens, p.B, cap, p.window, 0, &T, &unused, scratch);
   T *= HU;
   // Never more shares than tiles, so every share is non-empty and the shares
   // overlapping a unit form one run of consecutive workgroups.
@@ -162,13 +169,15 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_split_kernel(DecodeParam
 
   int b;
   long long bstart;
-  find_seq(p.lens, p.B, cap, HU, t_begin, &b, &bstart, scratch);
+  find_seq(p.lens, p.B, cap, p.window, HU, t_begin, &b, &bstart, scratch);
 
   const uint32_t flip = p.negate_q ? 0x80008000u : 0u;
   long long t = t_begin;
   while (t < t_end && b < p.B) {
     const int Lb = clamp_len(p.lens, b, cap);
-    const int Tb = tiles_of(Lb);
+    const int Tb = tiles_of(Lb, p.window);
+    const int ft = first_tile(Lb, p.window);                   // unit tile tt is key tile ft + tt
+    const int klo = p.window > 0 ? max(0, Lb - p.window) : 0;  // keys j < klo are outside
     const long long bend = bstart + HU * Tb;
     if (Tb == 0 || t >= bend) {
       bstart = bend;
@@ -184,7 +193,7 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_split_kernel(DecodeParam
     const int nh = min(32, p.g - qb * 32);
     const int u = (b * p.Hkv + kvh) * p.nqb + qb;
 
-    const size_t cache_off = ((size_t)(b * p.Hkv + kvh) * cap) * D;
+    const size_t cache_off = PAGED ? 0 : ((size_t)(b * p.Hkv + kvh) * cap) * D;
     const uint16_t* kb_ = static_cast<const uint16_t*>(p.kc) + cache_off;
     const uint16_t* vb_ = static_cast<const uint16_t*>(p.vc) + cache_off;
 
@@ -205,10 +214,26 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_split_kernel(DecodeParam
     const uint32_t row_b = D * 2;
     const uint32_t k_lane = l32 * row_b + hh * 16;
     const uint32_t v_lane = (4 * hh) * row_b + DPL * 2 * l32;
+    // Element offset of unit tile tt's first key row and the bytes of its valid rows. A
+    // paged cache looks the tile's page up in the block table (a tile never straddles
+    // pages); a page id outside the pool leaves no valid bytes, so its rows read as zeros.
+    auto tile_src = [&](int tt, uint32_t* valid) -> size_t {
+      const int j0 = (ft + tt) * DC_TILE;
+      const int nv = max(min(Lb - j0, DC_TILE), 0);
+      if constexpr (PAGED) {
+        const int page = p.block_table[(size_t)b * p.max_blocks + j0 / p.page_size];
+        const bool ok = page >= 0 && page < p.num_pages;
+        *valid = ok ? (uint32_t)nv * row_b : 0u;
+        return ok ? (((size_t)page * p.Hkv + kvh) * p.page_size + j0 % p.page_size) * D : 0;
+      } else {
+        *valid = (uint32_t)nv * row_b;
+        return (size_t)j0 * D;
+      }
+    };
     auto rsrc = [&](const uint16_t* base, int tt) {
-      const int j0 = tt * DC_TILE;
-      const uint32_t valid = (uint32_t)max(Lb - j0, 0) * row_b;
-      return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)j0 * D), 0, valid, 0x00020000);
+      uint32_t valid;
+      const size_t off = tile_src(tt, &valid);
+      return __builtin_amdgcn_make_buffer_rsrc((void*)(base + off), 0, valid, 0x00020000);
     };
     auto load_k = [&](TileRegs& r, int tt) {
       const __amdgpu_buffer_rsrc_t rk = rsrc(kb_, tt);
@@ -252,8 +277,10 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_split_kernel(DecodeParam
       }
     }
     __syncthreads();
+    float beta = 0.f;  // ALiBi slope of this lane's head in raw-score units
+    if constexpr (ALIBI) beta = l32 < nh ? p.alibi[hbase + l32] * kLog2e / c : 0.f;
     auto compute_tile = [&](TileRegs& r, int tt, bool more) {
-      const int j0 = tt * DC_TILE;
+      const int j0 = (ft + tt) * DC_TILE;
       f32x16 s = zero16();
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
@@ -261,12 +288,18 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_split_kernel(DecodeParam
         s = mfma_bf16_32x32x16(as_bf16x8(r.kf[ks]), as_bf16x8(qv), s);
       }
       if (more) load_k(r, tt + DC_WAVES);  // K registers are free again: fetch the next tile
-      const bool need_mask = j0 + DC_TILE > Lb;
+      if constexpr (ALIBI) {  // the query sits at L_b - 1: bias -slope * (L_b - 1 - j)
+        const float dq = (float)(Lb - 1 - j0 - 4 * hh);
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr)
+          s[rr] = fmaf(-beta, dq - (float)(8 * (rr >> 2) + (rr & 3)), s[rr]);
+      }
+      const bool need_mask = j0 + DC_TILE > Lb || j0 < klo;
       if (need_mask) {
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
           const int j = j0 + 8 * (rr >> 2) + 4 * hh + (rr & 3);
-          if (j >= Lb) s[rr] = -INFINITY;
+          if (j >= Lb || j < klo) s[rr] = -INFINITY;
         }
       }
       float mx = -INFINITY;
@@ -403,9 +436,9 @@ __global__ __launch_bounds__(CB_THREADS) void decode_combine_kernel(DecodeParams
   const int cap = p.max_len;
   const long long HU = (long long)p.Hkv * p.nqb;
   long long T, before;
-  tile_prefix<CB_THREADS>(p.lens, p.B, cap, b, &T, &before, scratch);
+  tile_prefix<CB_THREADS>(p.lens, p.B, cap, p.window, b, &T, &before, scratch);
   T *= HU;
-  const int Tb = tiles_of(clamp_len(p.lens, b, cap));
+  const int Tb = tiles_of(clamp_len(p.lens, b, cap), p.window);
   const int hbase = kvh * p.g + qb * 32;
   const int nh = min(32, p.g - qb * 32);
   const int n = blockIdx.y * HPB + threadIdx.x / TPH;
@@ -462,12 +495,12 @@ __global__ __launch_bounds__(CB_THREADS) void decode_combine_kernel(DecodeParams
   if (lse_out && d0 == 0) *lse_out = den > 0.f ? m + logf(den) : -INFINITY;
 }
 
-template <int D>
+template <int D, bool ALIBI, bool PAGED>
 hipError_t launch_d(const DecodeParams& p, bool need_combine, hipStream_t stream) {
   using Lay = DcLayout<D>;
   const size_t lds = Lay::Q_BYTES + (Lay::O_FLOATS + 2 * DC_WAVES * 32) * sizeof(float) +
                      (DC_WAVES + 4) * sizeof(long long);
-  auto kern = decode_split_kernel<D>;
+  auto kern = decode_split_kernel<D, ALIBI, PAGED>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -481,12 +514,22 @@ hipError_t launch_d(const DecodeParams& p, bool need_combine, hipStream_t stream
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_opts(const DecodeParams& p, bool need_combine, hipStream_t stream) {
+  const bool paged = p.block_table != nullptr;
+  if (p.alibi)
+    return paged ? launch_d<D, true, true>(p, need_combine, stream)
+                 : launch_d<D, true, false>(p, need_combine, stream);
+  return paged ? launch_d<D, false, true>(p, need_combine, stream)
+               : launch_d<D, false, false>(p, need_combine, stream);
+}
+
 }  // namespace
 
 hipError_t launch_decode_bf16(const DecodeParams& p, bool need_combine, hipStream_t stream) {
   switch (p.d) {
-    case 64: return launch_d<64>(p, need_combine, stream);
-    case 128: return launch_d<128>(p, need_combine, stream);
+    case 64: return launch_opts<64>(p, need_combine, stream);
+    case 128: return launch_opts<128>(p, need_combine, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -77,17 +77,20 @@ const char* gqa_status_string(int status) {
   }
 }
 
-int gqa_prefill(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
-                const int32_t* seqlens, int B, int S, int Hq, int Hkv, int d,
-                float softmax_scale, int causal, void* stream) {
+int gqa_prefill_ex(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+                   const int32_t* seqlens, int B, int S, int Hq, int Hkv, int d,
+                   float softmax_scale, int causal, int window, const float* alibi_slopes,
+                   void* stream) {
   if (B <= 0 || S <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return GQA_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return GQA_ERR_INVALID_ARG;
   if (!q || !k || !v || !o) return GQA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return GQA_ERR_INVALID_ARG;
-  if ((lse && ((uintptr_t)lse & 3u)) || (seqlens && ((uintptr_t)seqlens & 3u)))
+  if ((lse && ((uintptr_t)lse & 3u)) || (seqlens && ((uintptr_t)seqlens & 3u)) ||
+      (alibi_slopes && ((uintptr_t)alibi_slopes & 3u)))
     return GQA_ERR_INVALID_ARG;
   if (!isfinite(softmax_scale)) return GQA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return GQA_ERR_INVALID_ARG;
+  if (window < 0) return GQA_ERR_INVALID_ARG;
   if (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16) return GQA_ERR_UNSUPPORTED;
   if (!supported_prefill_d(dtype, d)) return GQA_ERR_UNSUPPORTED;
   const int g = Hq / Hkv;
@@ -100,6 +103,9 @@ int gqa_prefill(int dtype, const void* q, const void* k, const void* v, void* o,
   gqa::PrefillParams p;
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse; p.seqlens = seqlens;
   p.B = B; p.S = S; p.Hq = Hq; p.Hkv = Hkv; p.g = g; p.d = d;
+  p.window = window < S ? window : 0;  // a window of S or more keys hides nothing
+  p.alibi = alibi_slopes;
+  if (p.window > 0 && !causal) return GQA_ERR_UNSUPPORTED;
   p.scale_abs = fabsf(softmax_scale);
   // A zero scale (uniform weights) still gets a positive exponent factor, tiny enough
   // that every valid weight rounds to exp2(0) = 1 while masked scores (-inf) give 0.
@@ -125,6 +131,13 @@ int gqa_prefill(int dtype, const void* q, const void* k, const void* v, void* o,
   return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 
+int gqa_prefill(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+                const int32_t* seqlens, int B, int S, int Hq, int Hkv, int d,
+                float softmax_scale, int causal, void* stream) {
+  return gqa_prefill_ex(dtype, q, k, v, o, lse, seqlens, B, S, Hq, Hkv, d, softmax_scale, causal,
+                        0, nullptr, stream);
+}
+
 size_t gqa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_len, int num_splits) {
   DecodePlan plan;
   if (!plan_decode(B, Hq, Hkv, d, max_len, num_splits, &plan)) return 0;
@@ -137,19 +150,29 @@ int gqa_decode_num_workgroups(int B, int Hq, int Hkv, int max_len, int num_split
   return plan.n_wg;
 }
 
-int gqa_decode(int dtype, const void* q, const void* k_cache, const void* v_cache,
-               const int32_t* cache_lens, void* o, float* lse, int B, int Hq, int Hkv, int d,
-               int max_len, float softmax_scale, int num_splits, void* workspace,
-               size_t workspace_bytes, void* stream) {
+int gqa_decode_ex(int dtype, const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* cache_lens, const int32_t* block_table, int page_size,
+                  int max_blocks, int num_pages, void* o, float* lse, int B, int Hq, int Hkv,
+                  int d, int max_len, float softmax_scale, int window,
+                  const float* alibi_slopes, int num_splits, void* workspace,
+                  size_t workspace_bytes, void* stream) {
   DecodePlan plan;
   if (!plan_decode(B, Hq, Hkv, d > 0 ? d : 1, max_len, num_splits, &plan))
     return GQA_ERR_INVALID_ARG;
   if (!q || !k_cache || !v_cache || !o) return GQA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
     return GQA_ERR_INVALID_ARG;
-  if ((lse && ((uintptr_t)lse & 3u)) || (cache_lens && ((uintptr_t)cache_lens & 3u)))
+  if ((lse && ((uintptr_t)lse & 3u)) || (cache_lens && ((uintptr_t)cache_lens & 3u)) ||
+      (alibi_slopes && ((uintptr_t)alibi_slopes & 3u)) ||
+      (block_table && ((uintptr_t)block_table & 3u)))
     return GQA_ERR_INVALID_ARG;
-  if (!isfinite(softmax_scale)) return GQA_ERR_INVALID_ARG;
+  if (!isfinite(softmax_scale) || window < 0) return GQA_ERR_INVALID_ARG;
+  if (block_table) {
+    // Paged cache: tiles of 32 keys must not straddle pages, and the table covers max_len.
+    if (page_size <= 0 || page_size % kDecodeTile != 0 || max_blocks <= 0 || num_pages <= 0 ||
+        (long long)page_size * max_blocks != max_len)
+      return GQA_ERR_INVALID_ARG;
+  }
   if (dtype != GQA_DTYPE_BF16) return GQA_ERR_UNSUPPORTED;
   if (!supported_decode_d(d)) return GQA_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < plan.ws_bytes || !aligned16(workspace))
@@ -166,11 +189,26 @@ int gqa_decode(int dtype, const void* q, const void* k_cache, const void* v_cach
   // that every valid weight rounds to exp2(0) = 1 while masked scores (-inf) give 0.
   p.scale_log2 = fmaxf(p.scale_abs * kLog2e, kMinScaleLog2);
   p.negate_q = softmax_scale < 0.f ? 1 : 0;
+  p.window = window < max_len ? window : 0;  // a window of max_len or more keys hides nothing
+  p.alibi = alibi_slopes;
+  p.block_table = block_table;
+  p.page_size = block_table ? page_size : 0;
+  p.max_blocks = block_table ? max_blocks : 0;
+  p.num_pages = block_table ? num_pages : 0;
   // With no length array every unit has the same tile count; one share per unit then
   // maps each workgroup onto exactly one whole unit and no merge pass is needed.
   const bool need_combine = !(cache_lens == nullptr && plan.n_wg == plan.n_units);
   hipError_t e = gqa::launch_decode_bf16(p, need_combine, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+int gqa_decode(int dtype, const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* cache_lens, void* o, float* lse, int B, int Hq, int Hkv, int d,
+               int max_len, float softmax_scale, int num_splits, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  return gqa_decode_ex(dtype, q, k_cache, v_cache, cache_lens, nullptr, 0, 0, 0, o, lse, B, Hq,
+                       Hkv, d, max_len, softmax_scale, 0, nullptr, num_splits, workspace,
+                       workspace_bytes, stream);
 }
 
 }  // extern "C"

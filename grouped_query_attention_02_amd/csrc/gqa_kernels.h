@@ -25,6 +25,8 @@ struct PrefillParams {
   int n_wg;           // B * Hkv * nrb
   int per_xcd;        // workgroups per XCD queue
   int lpt;            // 1: deal (b, kvh) units to XCDs longest sequence first (needs seqlens)
+  int window;         // > 0: key j is visible to query i only if j > i - window
+  const float* alibi; // [Hq] ALiBi slopes (score -= slope * |i - j|), or null
 };
 
 // Largest batch for which the bf16 prefill orders its work by sequence length.
@@ -48,6 +50,12 @@ struct DecodeParams {
   float scale_log2;
   float scale_abs;
   int negate_q;
+  int window;                 // > 0: only the last `window` keys (j > L_b - 1 - window)
+  const float* alibi;         // [Hq] ALiBi slopes (score -= slope * (L_b - 1 - j)), or null
+  const int32_t* block_table; // paged cache: [B, max_blocks] page ids, or null (contiguous)
+  int page_size;              // keys per page (multiple of 32)
+  int max_blocks;             // columns of block_table
+  int num_pages;              // pages in each of the K and V pools
 };
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, int causal, hipStream_t stream);

@@ -113,7 +113,7 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool WINDOW, bool ALIBI>
 __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) void prefill_bf16_kernel(
     PrefillParams p) {
   using Lay = PfLayout<D>;
@@ -207,6 +207,18 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
   const int lim = CAUSAL ? min(Lb, qi + 1) : Lb;  // keys j < lim are visible to this row
   const int ntiles = (kv_end + PF_BN - 1) / PF_BN;
   const int wave_nt = (wave_kv_end + PF_BN - 1) / PF_BN;
+  // Sliding window: key j is also required to satisfy j >= lo = i - window + 1. Tiles
+  // below the lowest row's bound are skipped (the workgroup's and each wave's own).
+  constexpr int kNoLo = -(1 << 30);
+  int lo = kNoLo, t_first = 0, wave_t0 = 0, wave_lo_hi = kNoLo;
+  if constexpr (WINDOW) {
+    lo = qi - p.window + 1;
+    t_first = max(0, f0 / g - p.window + 1) / PF_BN;
+    if (fw < R) {
+      wave_t0 = max(0, fw / g - p.window + 1) / PF_BN;
+      wave_lo_hi = min(fw + 31, R - 1) / g - p.window + 1;  // highest bound in the wave
+    }
+  }
 
   // Q^T as the B operand: lane holds query row f, d = ks*16 + hh*8 .. +7.
   bf16x8 qf[D / 16];
@@ -310,43 +322,81 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
   };
 
   // ---- online softmax state (one query row per lane; lanes l and l^32 share a row)
-  float m_run = 0.f, l_run = 0.f;
+  // With a window, m_run stays -inf until the row sees a key; otherwise key 0 is visible to
+  // every row and the first tile always sets it.
+  float m_run = WINDOW ? -INFINITY : 0.f, l_run = 0.f;
   const float c = p.scale_log2;
+  // ALiBi: the score gets -slope_h * |i - j|, i.e. -beta * |i - j| in the units of the raw
+  // dot product that c = |scale| * log2(e) scales into exp2 units.
+  float beta = 0.f;
+  if constexpr (ALIBI) beta = p.alibi[hq] * kLog2e / c;
 
-  // Key j = t0 + 32kb + 8(r/4) + 4hh + (r%4) is kept iff j < lim: the sign of j - lim
-  // selects between the score and -inf bit patterns (no compare masks in SGPRs).
+  // Key j = t0 + 32kb + 8(r/4) + 4hh + (r%4) is kept iff lo <= j < lim: the signs of
+  // j - lim and j - lo select between the score and -inf bit patterns (no compare masks
+  // in SGPRs).
   auto mask = [&](f32x16 (&s)[NKB], int t0) {
     const int base = t0 + 4 * hh - lim;
+    const int base_lo = t0 + 4 * hh - lo;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const uint32_t keep = (uint32_t)((base + 32 * kb + 8 * (r >> 2) + (r & 3)) >> 31);
+        const int jj = 32 * kb + 8 * (r >> 2) + (r & 3);
+        uint32_t keep = (uint32_t)((base + jj) >> 31);
+        if constexpr (WINDOW) keep &= ~(uint32_t)((base_lo + jj) >> 31);
         s[kb][r] = __uint_as_float((__float_as_uint(s[kb][r]) & keep) | (0xff800000u & ~keep));
       }
   };
-  // Row max over the tile (the other keys of this row sit in lane l ^ 32).
-  auto row_max = [&](const f32x16 (&s)[NKB]) {
+  // Mask tile t's scores if any key of the wave's rows is masked in it.
+  auto prep = [&](f32x16 (&s)[NKB], int t) {
+    const int t0 = t * PF_BN;
+    if (t0 + PF_BN > wave_mask_from || (WINDOW && t0 < wave_lo_hi)) mask(s, t0);
+  };
+  // ALiBi distance |i - j| of this lane's score (kb, r) in tile t: key j = t0 + 32kb +
+  // 8(r/4) + 4hh + (r%4), so i - j = dq(t) - (32kb + 8(r/4) + r%4).
+  // (The empty asm hides where dq came from, so the compiler recomputes the distances in
+  // each use instead of keeping 32 of them live between the row max and the weights.)
+  auto alibi_dq = [&](int t) {
+    float dq = (float)(qi - t * PF_BN - 4 * hh);
+    asm volatile("" : "+v"(dq));
+    return dq;
+  };
+  auto alibi_off = [](int kb, int r) { return (float)(32 * kb + 8 * (r >> 2) + (r & 3)); };
+  // Row max of the (biased) scores over the tile (the row's other keys sit in lane l ^ 32).
+  auto row_max = [&](const f32x16 (&s)[NKB], int t) {
     float mx = -INFINITY;
+    const float dq = ALIBI ? alibi_dq(t) : 0.f;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      for (int r = 0; r < 16; ++r) {
+        float x = s[kb][r];
+        if constexpr (ALIBI) x = fmaf(-beta, fabsf(dq - alibi_off(kb, r)), x);
+        mx = fmaxf(mx, x);
+      }
     return pair_max(mx);
   };
   // Weights exp2(c s - c m) rounded to bf16 as the PV operand; returns this lane's sum of
   // the rounded weights (the same values the PV product uses). exp2(-inf) = 0.
   const bf16x2 ones2 = __builtin_bit_cast(bf16x2, 0x3f803f80u);
-  auto weights = [&](const f32x16 (&s)[NKB], bf16x8 (&pp)[NKS]) {
-    const float msc = m_run * c;
+  auto weights = [&](const f32x16 (&s)[NKB], bf16x8 (&pp)[NKS], int t) {
+    const float msc = ((WINDOW && m_run == -INFINITY) ? 0.f : m_run) * c;  // no key yet
+    const float dq = ALIBI ? alibi_dq(t) : 0.f;
+    const float bc = beta * c;  // the bias slope in exp2 units
+    // exp2 argument of score (kb, r): c * (s - beta |i - j|) - c * m
+    auto arg = [&](int kb, int r) {
+      float x = fmaf(s[kb][r], c, -msc);
+      if constexpr (ALIBI) x = fmaf(-bc, fabsf(dq - alibi_off(kb, r)), x);
+      return x;
+    };
     float lsum = 0.f;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       u32x4 u;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const f32x2 e = {fast_exp2(fmaf(s[ks >> 1][8 * (ks & 1) + 2 * i], c, -msc)),
-                         fast_exp2(fmaf(s[ks >> 1][8 * (ks & 1) + 2 * i + 1], c, -msc))};
+        const int kb = ks >> 1, r0 = 8 * (ks & 1) + 2 * i;
+        const f32x2 e = {fast_exp2(arg(kb, r0)), fast_exp2(arg(kb, r0 + 1))};
         const bf16x2 h = __builtin_convertvector(e, bf16x2);
         u[i] = __builtin_bit_cast(uint32_t, h);
         // The dot operand is the converted pair itself: bit-casting it back out of u[i]
@@ -358,38 +408,41 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
     return lsum;
   };
 
-  // The exponent offset m_run is the row max of the first tile and stays fixed while every
-  // weight of a tile is at most 2^kTau (checked through the tile's weight sum, which bounds
-  // each weight). A tile that breaks this (scores grown past the offset) is redone with
-  // the offset raised to its row max, after rescaling what was accumulated. Every term of
-  // a row always shares one offset, so the normalised result is that of the exact max.
+  // The exponent offset m_run is the row max of the first tile in which the row sees a
+  // key, and stays fixed while every weight of a tile is at most 2^32 (checked through the
+  // tile's weight sum, which bounds each weight). A tile that breaks this (scores grown
+  // past the offset) is redone with the offset raised to its row max, after rescaling what
+  // was accumulated. Every term of a row always shares one offset, so the normalised
+  // result is that of the exact max.
   auto tile = [&](int t) {
     f32x16 s[NKB];
     qk(s, kslot(t));
-    const int t0 = t * PF_BN;
-    const bool masked = t0 + PF_BN > wave_mask_from;
-    if (masked) mask(s, t0);
-    if (t == 0) {
-      const float mx = row_max(s);     // key 0 is visible to every row, so mx is finite
-      m_run = mx == -INFINITY ? 0.f : mx;
+    prep(s, t);
+    if constexpr (WINDOW) {
+      if (wave_any(m_run == -INFINITY)) {  // rows that have not seen a key yet
+        const float mx = row_max(s, t);
+        if (m_run == -INFINITY) m_run = mx;  // stays -inf while all the row's keys are masked
+      }
+    } else if (t == 0) {
+      m_run = row_max(s, t);  // key 0 is visible to every row, so this is finite
     }
     bf16x8 pp[NKS];
-    float lsum = weights(s, pp);
+    float lsum = weights(s, pp, t);
     if (wave_any(!(lsum <= kSumCap))) {
       // Recompute the scores from the K tile (still in LDS) rather than keeping them live
       // through the common path: the empty asm keeps the compiler from reusing them.
       asm volatile("" ::: "memory");
       qk(s, kslot(t));
-      if (masked) mask(s, t0);
-      const float m_new = fmaxf(m_run, row_max(s));
-      const float alpha = fast_exp2((m_run - m_new) * c);
+      prep(s, t);
+      const float m_new = fmaxf(m_run, row_max(s, t));
+      const float alpha = m_new == m_run ? 1.f : fast_exp2((m_run - m_new) * c);
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
       m_run = m_new;
-      lsum = weights(s, pp);
+      lsum = weights(s, pp, t);
     }
     l_run += lsum;
     pv(pp, vslot(t));
@@ -397,19 +450,20 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
 
   // ---- pipeline: the DMA of tile t+3 is issued before tile t is computed; after tile t
   // each wave waits for its own copies of tile t+1 and the barrier publishes everyone's.
-  if (ntiles > 0) {
+  const bool any_tile = t_first < ntiles;
+  if (any_tile) {
 #pragma unroll
-    for (int t = 0; t < kAhead; ++t) issue_tile(t);
-    wait_vm<kJ * (kAhead - 1)>();  // tile 0 has landed
+    for (int t = 0; t < kAhead; ++t) issue_tile(t_first + t);
+    wait_vm<kJ * (kAhead - 1)>();  // the first tile has landed
   }
   block_barrier();
-  for (int t = 0; t < ntiles; ++t) {
+  for (int t = t_first; t < ntiles; ++t) {
     issue_tile(t + kAhead);  // past the end: empty resource, zeros land in a free slot
-    if (t < wave_nt) tile(t);
+    if (t >= wave_t0 && t < wave_nt) tile(t);
     wait_vm<kJ * kAhead - kJ>();  // this wave's copies of tile t+1 have landed
     block_barrier();              // ... and every wave's; slot t may be overwritten next
   }
-  if (ntiles > 0) wait_vm<0>();  // drain the copies issued for tiles past the end
+  if (any_tile) wait_vm<0>();  // drain the copies issued for tiles past the end
 
   // Epilogue: O = O^T / l, rounded to bf16; LSE = m*|scale| + ln l.
   const float l_tot = pair_sum(l_run);
@@ -432,15 +486,29 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool WINDOW, bool ALIBI>
 hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
   const size_t lds = PfLayout<D>::LDS_BYTES;
-  auto kern = prefill_bf16_kernel<D, CAUSAL>;
+  auto kern = prefill_bf16_kernel<D, CAUSAL, WINDOW, ALIBI>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(8 * p.per_xcd), dim3(PfShape<D>::THREADS), lds, stream, p);
   return hipGetLastError();
+}
+
+// The sliding window is built for causal attention only (the host rejects it otherwise).
+template <int D>
+hipError_t launch_d(const PrefillParams& p, int causal, hipStream_t stream) {
+  const bool al = p.alibi != nullptr;
+  if (!causal)
+    return al ? launch_one<D, false, false, true>(p, stream)
+              : launch_one<D, false, false, false>(p, stream);
+  if (p.window > 0)
+    return al ? launch_one<D, true, true, true>(p, stream)
+              : launch_one<D, true, true, false>(p, stream);
+  return al ? launch_one<D, true, false, true>(p, stream)
+            : launch_one<D, true, false, false>(p, stream);
 }
 
 }  // namespace
@@ -451,9 +519,9 @@ int prefill_rows_per_wg_bf16(int d) {
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, int causal, hipStream_t stream) {
   switch (p.d) {
-    case 32: return causal ? launch_one<32, true>(p, stream) : launch_one<32, false>(p, stream);
-    case 64: return causal ? launch_one<64, true>(p, stream) : launch_one<64, false>(p, stream);
-    case 128: return causal ? launch_one<128, true>(p, stream) : launch_one<128, false>(p, stream);
+    case 32: return launch_d<32>(p, causal, stream);
+    case 64: return launch_d<64>(p, causal, stream);
+    case 128: return launch_d<128>(p, causal, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -64,6 +64,19 @@ __global__ __launch_bounds__(PF32_THREADS) void prefill_f32_kernel(PrefillParams
   }
   const int lim = CAUSAL ? min(Lb, qi + 1) : Lb;
   const int ntiles = (kv_end + PF32_BN - 1) / PF32_BN;
+  // Sliding window: keys j >= lo = i - window + 1 only; tiles below every row's bound are
+  // skipped. ALiBi: the score gets -slope_h * |i - j| (beta: the slope in raw-score units).
+  constexpr int kNoLo = -(1 << 30);
+  int lo = kNoLo, t_first = 0, wave_lo_min = kNoLo, wave_lo_hi = kNoLo;
+  if (p.window > 0) {
+    lo = qi - p.window + 1;
+    t_first = max(0, f0 / g - p.window + 1) / PF32_BN;
+    if (fw < R) {
+      wave_lo_min = fw / g - p.window + 1;
+      wave_lo_hi = min(fw + 31, R - 1) / g - p.window + 1;
+    }
+  }
+  const float beta = p.alibi ? p.alibi[hq] * kLog2e / p.scale_log2 : 0.f;
 
   // B operand of S^T = K Q^T: lane holds Q[row][2*ks + hh].
   float qf[D / 2];
@@ -85,7 +98,7 @@ __global__ __launch_bounds__(PF32_THREADS) void prefill_f32_kernel(PrefillParams
   const float c = p.scale_log2;
   constexpr int CPR = D / 4;  // float4 chunks per row
 
-  for (int t = 0; t < ntiles; ++t) {
+  for (int t = t_first; t < ntiles; ++t) {
     const int t0 = t * PF32_BN;
     __syncthreads();  // previous tile fully consumed
     for (int ch = tid; ch < PF32_BN * CPR; ch += PF32_THREADS) {
@@ -98,18 +111,25 @@ __global__ __launch_bounds__(PF32_THREADS) void prefill_f32_kernel(PrefillParams
       *reinterpret_cast<u32x4*>(vs_ + key * VSTR + col * 4) = vv;
     }
     __syncthreads();
-    if (t0 >= wave_kv_end) continue;
+    if (t0 >= wave_kv_end || t0 + PF32_BN <= wave_lo_min) continue;
 
     f32x16 s = zero16();
 #pragma unroll
     for (int ks = 0; ks < D / 2; ++ks) s = mfma_f32_32x32x2(ks_[l32 * KSTR + 2 * ks + hh], qf[ks], s);
 
-    const bool need_mask = t0 + PF32_BN > wave_mask_from;
+    if (p.alibi) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = t0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        s[r] = fmaf(-beta, fabsf((float)(qi - j)), s[r]);
+      }
+    }
+    const bool need_mask = t0 + PF32_BN > wave_mask_from || t0 < wave_lo_hi;
     if (need_mask) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int j = t0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (j >= lim) s[r] = -INFINITY;
+        if (j >= lim || j < lo) s[r] = -INFINITY;
       }
     }
     float mx = -INFINITY;

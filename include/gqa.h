@@ -92,6 +92,30 @@ int gqa_prefill(int dtype, const void *q, const void *k, const void *v, void *o,
                 float softmax_scale, int causal, void *stream);
 
 /*
+ * gqa_prefill_ex - gqa_prefill with two optional score modifiers.
+ *
+ *   window         0: none. w > 0 (causal only): query i sees only keys
+ *                  j > i - w, i.e. its own key and the w - 1 before it (the
+ *                  sliding window of Mistral-style models, which the
+ *                  azimuth.plus GQA digest's timeline pairs with GQA, entry
+ *                  "2023: Mistral 7B"). Key tiles outside every row's window
+ *                  are skipped. A window of S or more keys changes nothing.
+ *   alibi_slopes   [Hq] fp32 device array, or NULL. The score of query i and
+ *                  key j in head h becomes softmax_scale * <q_i, k_j> -
+ *                  alibi_slopes[h] * |i - j| before the softmax (the pages'
+ *                  attention signature has an `alibi_slopes` argument, gitcode
+ *                  page, section "GQA的分组共享机制"; the bias form is the usual
+ *                  ALiBi one). The LSE output includes the bias.
+ * Every other argument is as for gqa_prefill. Additionally returns
+ * GQA_ERR_INVALID_ARG for window < 0 or a misaligned alibi_slopes, and
+ * GQA_ERR_UNSUPPORTED for a window on non-causal attention.
+ */
+int gqa_prefill_ex(int dtype, const void *q, const void *k, const void *v, void *o, float *lse,
+                   const int32_t *seqlens, int B, int S, int Hq, int Hkv, int d,
+                   float softmax_scale, int causal, int window, const float *alibi_slopes,
+                   void *stream);
+
+/*
  * gqa_decode_workspace_bytes - device workspace gqa_decode needs for these
  * arguments (split partials: normalised fp32 outputs and their log-sum-exp).
  * Returns 0 for invalid arguments.
@@ -142,6 +166,40 @@ int gqa_decode(int dtype, const void *q, const void *k_cache, const void *v_cach
                const int32_t *cache_lens, void *o, float *lse, int B, int Hq, int Hkv, int d,
                int max_len, float softmax_scale, int num_splits, void *workspace,
                size_t workspace_bytes, void *stream);
+
+/*
+ * gqa_decode_ex - gqa_decode over a contiguous or paged KV cache, with an
+ * optional sliding window and ALiBi bias. The query is the token at position
+ * cache_lens[b] - 1.
+ *
+ *   block_table    NULL: k_cache, v_cache are [B, Hkv, max_len, d] as for
+ *                  gqa_decode. Otherwise a paged cache (the azimuth.plus GQA
+ *                  digest, "the bigger picture": GQA composes with paged
+ *                  attention): k_cache and v_cache are page pools
+ *                  [num_pages, Hkv, page_size, d] and block_table is a
+ *                  [B, max_blocks] int32 device array; key j of sequence b is
+ *                  row j % page_size of page block_table[b][j / page_size].
+ *                  Entries past a sequence's length are never read; a page id
+ *                  outside [0, num_pages) reads as zeros (no fault).
+ *   page_size      keys per page, a positive multiple of 32 (paged only).
+ *   max_blocks     columns of block_table; max_len must equal
+ *                  max_blocks * page_size (paged only).
+ *   num_pages      pages in each pool (paged only).
+ *   window         0: none. w > 0: only the last w keys of each sequence
+ *                  (j > cache_lens[b] - 1 - w) are attended; the work split
+ *                  covers only those keys.
+ *   alibi_slopes   [Hq] fp32 device array, or NULL: the score of key j becomes
+ *                  softmax_scale * <q, k_j> - alibi_slopes[h] * (L_b - 1 - j).
+ * Every other argument is as for gqa_decode (the workspace size is the same).
+ * Additionally returns GQA_ERR_INVALID_ARG for window < 0, misaligned
+ * alibi_slopes or block_table, or inconsistent paging arguments.
+ */
+int gqa_decode_ex(int dtype, const void *q, const void *k_cache, const void *v_cache,
+                  const int32_t *cache_lens, const int32_t *block_table, int page_size,
+                  int max_blocks, int num_pages, void *o, float *lse, int B, int Hq, int Hkv,
+                  int d, int max_len, float softmax_scale, int window,
+                  const float *alibi_slopes, int num_splits, void *workspace,
+                  size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

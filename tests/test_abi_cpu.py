@@ -111,3 +111,51 @@ def test_decode_plan_rule(lib):
     assert gqa.decode_workspace_bytes(32, 32, 1, 128, 32768, 0) == (W + U) * 32 * 129 * 4
     assert gqa.decode_workspace_bytes(32, 32, 1, 128, 0, 0) == 0
     assert gqa.decode_workspace_bytes(32, 30, 4, 128, 100, 0) == 0
+
+
+def _prefill_ex(lib, window=0, slopes=None, causal=1, **kw):
+    a = dict(dtype=BF16, q=P, k=P, v=P, o=P, lse=None, lens=None, B=2, S=64, Hq=8, Hkv=2, d=64,
+             scale=0.125)
+    a.update(kw)
+    return lib.gqa_prefill_ex(a["dtype"], a["q"], a["k"], a["v"], a["o"], a["lse"], a["lens"],
+                              a["B"], a["S"], a["Hq"], a["Hkv"], a["d"], a["scale"], causal,
+                              window, slopes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(window=-1), INV),
+    (dict(slopes=P + 2), INV),            # misaligned slope array
+    (dict(window=8, causal=0), UNS),      # the window is the causal (sliding) form only
+    (dict(window=4, Hq=6, Hkv=4), INV),   # the ordinary checks still apply
+    (dict(window=4, d=48), UNS),
+])
+def test_prefill_ex_rejects(lib, kw, code):
+    assert _prefill_ex(lib, **kw) == code
+
+
+def _decode_ex(lib, table=None, page=0, blocks=0, pages=0, window=0, slopes=None, max_len=1024,
+               ws_bytes=None, **kw):
+    a = dict(dtype=BF16, q=P, k=P, v=P, lens=None, o=P, lse=None, B=4, Hq=32, Hkv=1, d=128,
+             scale=0.1, splits=0, ws=P)
+    a.update(kw)
+    if ws_bytes is None:
+        ws_bytes = lib.gqa_decode_workspace_bytes(a["B"], a["Hq"], a["Hkv"], a["d"], max_len,
+                                                  a["splits"])
+    return lib.gqa_decode_ex(a["dtype"], a["q"], a["k"], a["v"], a["lens"], table, page, blocks,
+                             pages, a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["d"], max_len,
+                             a["scale"], window, slopes, a["splits"], a["ws"], ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(window=-3), INV),
+    (dict(slopes=P + 1), INV),
+    (dict(table=P + 2, page=64, blocks=16, pages=100), INV),  # misaligned table
+    (dict(table=P, page=48, blocks=16, pages=100, max_len=768), INV),  # page not a multiple of 32
+    (dict(table=P, page=64, blocks=16, pages=100, max_len=1000), INV),  # max_len != blocks * page
+    (dict(table=P, page=64, blocks=16, pages=0), INV),
+    (dict(table=P, page=0, blocks=16, pages=10), INV),
+    (dict(table=P, page=64, blocks=16, pages=10, dtype=F32), UNS),
+    (dict(table=P, page=64, blocks=16, pages=10, ws=None), WS),
+])
+def test_decode_ex_rejects(lib, kw, code):
+    assert _decode_ex(lib, **kw) == code

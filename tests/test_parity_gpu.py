@@ -4,10 +4,11 @@ Tolerances (max |O_gpu - O_oracle| over every checked element):
   fp32 inputs: 1e-5;  bf16 inputs with fp32 accumulation and bf16 output: 2e-2.
 LSE (natural log): 1e-4 for fp32 paths. bf16 decode: 1e-3 (the scores are exact
 products of the stored inputs accumulated in fp32 and the weight sums are fp32).
-bf16 prefill: 2.5e-3. Its weights are rounded to bf16 (relative error <= 2^-9 each)
-for the PV product and the row sum adds those same rounded weights, so the output is
-normalised by exactly the weights it uses, and the sum (of positive terms) is off by
-a relative 2^-9 at most: ln(1 + 2^-9) = 1.95e-3, plus fp32 rounding.
+bf16 prefill: 4e-3. Its weights are rounded to bf16 (8 significant bits, round to
+nearest: relative error <= 2^-8 each) for the PV product and the row sum adds those
+same rounded weights, so the output is normalised by exactly the weights it uses, and
+the sum (of positive terms) is off by a relative 2^-8 at most: ln(1 + 2^-8) = 3.9e-3,
+plus fp32 rounding.
 """
 import math
 import sys
@@ -22,7 +23,7 @@ import workloads as W
 pytestmark = pytest.mark.gpu
 
 TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-2}
-LSE_TOL = {torch.float32: 1e-4, torch.bfloat16: 2.5e-3}   # prefill
+LSE_TOL = {torch.float32: 1e-4, torch.bfloat16: 4e-3}   # prefill
 BF16_DECODE_LSE_TOL = 1e-3
 
 

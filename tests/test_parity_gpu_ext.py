@@ -1,0 +1,241 @@
+"""GPU parity of the optional score modifiers and the paged cache, through the C ABI
+(gqa_prefill_ex / gqa_decode_ex), against the fp64 oracle.
+
+Tolerances are those of test_parity_gpu.py: outputs 1e-5 (fp32) and 2e-2 (bf16);
+LSE 1e-4 (fp32), 4e-3 (bf16 prefill: the weights are summed after rounding to bf16,
+relative error <= 2^-8, so ln(1 + 2^-8) = 3.9e-3) and 1e-3 (bf16 decode).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import grouped_query_attention_02_amd as gqa
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-2}
+LSE_TOL = {torch.float32: 1e-4, torch.bfloat16: 4e-3}
+DEC_LSE_TOL = 1e-3
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu(built_lib):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gqa.load()
+
+
+def _rand(shape, seed, dtype, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g) * scale).to(dtype)
+
+
+def _errs(o, lse, ref_o, ref_l):
+    a = o.detach().double().cpu().numpy()
+    assert not np.isnan(a).any(), "NaN in GPU output"
+    e = float(np.abs(a - ref_o).max())
+    b = lse.detach().double().cpu().numpy()
+    fin = np.isfinite(ref_l)
+    assert np.array_equal(np.isfinite(b), fin), "LSE finiteness differs"
+    le = float(np.abs(b[fin] - ref_l[fin]).max()) if fin.any() else 0.0
+    return e, le
+
+
+def alibi_slopes(H):
+    """The usual geometric ALiBi slopes 2^(-8 k / H), k = 1..H."""
+    return [2.0 ** (-8.0 * (k + 1) / H) for k in range(H)]
+
+
+PREFILL_CASES = []
+for dtype in (torch.bfloat16, torch.float32):
+    for d in (32, 64, 128):
+        for (window, alibi, causal) in ((1, False, True), (17, False, True), (64, False, True),
+                                        (100, True, True), (0, True, True), (0, True, False)):
+            PREFILL_CASES.append((dtype, d, window, alibi, causal))
+
+
+@pytest.mark.parametrize("dtype,d,window,alibi,causal", PREFILL_CASES)
+def test_prefill_window_alibi(oracle_mod, dtype, d, window, alibi, causal):
+    B, S, Hq, Hkv = 3, 150, 8, 2
+    seed = 2000 + d + window + 7 * int(alibi) + int(causal)
+    _say(f"case prefill_ex {dtype} d={d} window={window} alibi={alibi} causal={causal}")
+    q, k, v = _rand((B, S, Hq, d), seed, dtype), _rand((B, S, Hkv, d), seed + 1, dtype), \
+        _rand((B, S, Hkv, d), seed + 2, dtype)
+    slopes = alibi_slopes(Hq) if alibi else None
+    scale = 1 / math.sqrt(d)
+    for lens in (None, [150, 3, 77]):
+        ld = None if lens is None else torch.tensor(lens, dtype=torch.int32, device="cuda")
+        o, lse = gqa.prefill(q.cuda(), k.cuda(), v.cuda(), causal=causal, softmax_scale=scale,
+                             seqlens=ld, window=window, alibi_slopes=slopes, return_lse=True)
+        torch.cuda.synchronize()
+        ro, rl = oracle_mod.prefill(q, k, v, scale=scale, causal=causal, seqlens=lens,
+                                    window=window, alibi_slopes=slopes)
+        e, le = _errs(o, lse, ro, rl)
+        _say(f"  lens={lens} max_abs_err={e:.3e} lse_err={le:.3e}")
+        assert e <= TOL[dtype] and le <= LSE_TOL[dtype]
+
+
+def test_prefill_window_full_size_sampled(oracle_mod):
+    """Causal Llama-shaped prefill (B=4, S=4096, 32/8 heads, d=128) with a 1000-key window and
+    ALiBi, in the launch configuration the benchmark uses; 300 sampled rows."""
+    w = W.WORKLOADS["llama_causal_prefill"]
+    x = W.make_prefill(w)
+    slopes = alibi_slopes(w.Hq)
+    _say("case llama_causal_prefill window=1000 + alibi (full size)")
+    o, lse = gqa.prefill(x["q"].cuda(), x["k"].cuda(), x["v"].cuda(), causal=True,
+                         softmax_scale=w.softmax_scale, window=1000, alibi_slopes=slopes,
+                         return_lse=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    rows = [(int(rng.integers(w.B)), int(rng.integers(w.Hq)), int(rng.integers(w.S)))
+            for _ in range(296)] + [(0, 0, 0), (1, 5, 999), (2, 31, 1000), (3, 17, w.S - 1)]
+    ro, rl = oracle_mod.prefill_rows(x["q"], x["k"], x["v"], rows, scale=w.softmax_scale,
+                                     causal=True, window=1000, alibi_slopes=slopes)
+    oc, lc = o.cpu(), lse.cpu()
+    got = torch.stack([oc[b, i, h] for b, h, i in rows])
+    got_l = torch.tensor([float(lc[b, h, i]) for b, h, i in rows], dtype=torch.float64)
+    e, le = _errs(got, got_l, ro, rl)
+    _say(f"  rows={len(rows)} max_abs_err={e:.3e} lse_err={le:.3e}")
+    assert e <= 2e-2 and le <= LSE_TOL[torch.bfloat16]
+
+
+def _paged(kc, vc, page_size, seed, extra=5, poison=True):
+    """Scatter [B, Hkv, max_len, d] caches into NaN-filled page pools with a random table."""
+    B, Hkv, max_len, d = kc.shape
+    mb = max_len // page_size
+    n = B * mb + extra
+    order = np.random.default_rng(seed).permutation(n)
+    table = torch.tensor(order[: B * mb].reshape(B, mb), dtype=torch.int32)
+    fill = float("nan") if poison else 0.0
+    kp = torch.full((n, Hkv, page_size, d), fill, dtype=kc.dtype)
+    vp = torch.full((n, Hkv, page_size, d), fill, dtype=vc.dtype)
+    for b in range(B):
+        for i in range(mb):
+            kp[table[b, i]] = kc[b, :, i * page_size:(i + 1) * page_size]
+            vp[table[b, i]] = vc[b, :, i * page_size:(i + 1) * page_size]
+    return kp, vp, table
+
+
+DECODE_CASES = []
+for d in (64, 128):
+    for (Hq, Hkv) in ((32, 1), (16, 2), (8, 8), (64, 2)):
+        for (window, alibi, page) in ((0, False, 32), (0, True, 0), (100, False, 0),
+                                      (33, True, 64), (0, False, 256), (257, True, 128)):
+            DECODE_CASES.append((d, Hq, Hkv, window, alibi, page))
+
+
+@pytest.mark.parametrize("d,Hq,Hkv,window,alibi,page", DECODE_CASES)
+def test_decode_window_alibi_paged(oracle_mod, d, Hq, Hkv, window, alibi, page):
+    B, max_len = 5, 768
+    seed = 3000 + d + Hq + Hkv + window + page + int(alibi)
+    _say(f"case decode_ex d={d} Hq={Hq} Hkv={Hkv} window={window} alibi={alibi} page={page}")
+    q = _rand((B, Hq, d), seed, torch.bfloat16)
+    kc = _rand((B, Hkv, max_len, d), seed + 1, torch.bfloat16)
+    vc = _rand((B, Hkv, max_len, d), seed + 2, torch.bfloat16)
+    lens = [768, 1, 0, 300, 513]
+    slopes = alibi_slopes(Hq) if alibi else None
+    if page:
+        kp, vp, table = _paged(kc, vc, page, seed)
+        args = dict(block_table=table.cuda(), page_size=page)
+        kd, vd = kp.cuda(), vp.cuda()
+    else:
+        args, kd, vd, table = {}, kc.cuda(), vc.cuda(), None
+    ref_o, ref_l = oracle_mod.decode(q, kc, vc, scale=0.09, lens=lens, window=window,
+                                     alibi_slopes=slopes)
+    outs = []
+    for splits in (0, 1, 3):
+        o, lse = gqa.decode(q.cuda(), kd, vd, torch.tensor(lens, dtype=torch.int32).cuda(),
+                            softmax_scale=0.09, num_splits=splits, window=window,
+                            alibi_slopes=slopes, return_lse=True, **args)
+        torch.cuda.synchronize()
+        e, le = _errs(o, lse, ref_o, ref_l)
+        _say(f"  splits={splits} max_abs_err={e:.3e} lse_err={le:.3e}")
+        assert e <= 2e-2 and le <= DEC_LSE_TOL
+        outs.append(o.float())
+    for o in outs[1:]:
+        assert (o - outs[0]).abs().max().item() <= 2e-2
+
+
+def test_paged_decode_matches_contiguous_bitwise():
+    """The paged kernel only changes where rows are read from: with the same split plan its
+    output equals the contiguous kernel's bit for bit."""
+    B, Hq, Hkv, d, max_len, page = 6, 32, 4, 128, 1024, 64
+    q = _rand((B, Hq, d), 41, torch.bfloat16)
+    kc = _rand((B, Hkv, max_len, d), 42, torch.bfloat16)
+    vc = _rand((B, Hkv, max_len, d), 43, torch.bfloat16)
+    lens = torch.tensor([1024, 5, 700, 64, 0, 999], dtype=torch.int32).cuda()
+    kp, vp, table = _paged(kc, vc, page, 44)
+    for window, slopes in ((0, None), (200, alibi_slopes(Hq))):
+        a = gqa.decode(q.cuda(), kc.cuda(), vc.cuda(), lens, window=window, alibi_slopes=slopes)
+        b = gqa.decode(q.cuda(), kp.cuda(), vp.cuda(), lens, window=window, alibi_slopes=slopes,
+                       block_table=table.cuda(), page_size=page)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("use_alibi", [False, True])
+def test_paged_decode_full_size_sampled(oracle_mod, use_alibi):
+    """MQA ragged decode (B=32, 32/1 heads, d=128, caches up to 32768) from a paged cache with
+    256-key pages scattered over the pool, in the benchmark's launch configuration."""
+    w = W.WORKLOADS["mqa_ragged_decode"]
+    x = W.make_decode(w)
+    page = 256
+    mb = w.max_len // page
+    n_pages = w.B * mb + 7
+    perm = np.random.default_rng(12).permutation(n_pages)
+    table = torch.tensor(perm[: w.B * mb].reshape(w.B, mb), dtype=torch.int32)
+    kc, vc = x["k_cache"], x["v_cache"]
+    kp = torch.zeros((n_pages, w.Hkv, page, w.d), dtype=kc.dtype)
+    vp = torch.zeros((n_pages, w.Hkv, page, w.d), dtype=vc.dtype)
+    kp[table.view(-1).long()] = kc.view(w.B, w.Hkv, mb, page, w.d).permute(0, 2, 1, 3, 4) \
+        .reshape(w.B * mb, w.Hkv, page, w.d)
+    vp[table.view(-1).long()] = vc.view(w.B, w.Hkv, mb, page, w.d).permute(0, 2, 1, 3, 4) \
+        .reshape(w.B * mb, w.Hkv, page, w.d)
+    slopes = alibi_slopes(w.Hq) if use_alibi else None
+    _say(f"case mqa_ragged_decode paged page={page} alibi={use_alibi} (full size)")
+    o, lse = gqa.decode(x["q"].cuda(), kp.cuda(), vp.cuda(), x["lens"].cuda(),
+                        softmax_scale=w.softmax_scale, alibi_slopes=slopes,
+                        block_table=table.cuda(), page_size=page, return_lse=True)
+    torch.cuda.synchronize()
+    pairs = [(b, h) for b in range(w.B) for h in (0, 13, 31)]
+    ro, rl = oracle_mod.decode_pairs(x["q"], kc, vc, pairs, scale=w.softmax_scale,
+                                     lens=x["lens"], alibi_slopes=slopes)
+    oc, lc = o.cpu(), lse.cpu()
+    got = torch.stack([oc[b, h] for b, h in pairs])
+    got_l = torch.tensor([float(lc[b, h]) for b, h in pairs], dtype=torch.float64)
+    e, le = _errs(got, got_l, ro, rl)
+    _say(f"  pairs={len(pairs)} max_abs_err={e:.3e} lse_err={le:.3e}")
+    assert e <= 2e-2 and le <= DEC_LSE_TOL
+
+
+def test_bad_page_ids_read_as_zeros():
+    """A page id outside the pool must not fault: its rows read as zeros (equal to a cache
+    whose rows there are zero)."""
+    B, Hq, Hkv, d, page, mb = 2, 8, 1, 64, 32, 4
+    q = _rand((B, Hq, d), 51, torch.bfloat16)
+    kc = _rand((B, Hkv, page * mb, d), 52, torch.bfloat16)
+    vc = _rand((B, Hkv, page * mb, d), 53, torch.bfloat16)
+    kp, vp, table = _paged(kc, vc, page, 54, poison=False)
+    bad = table.clone()
+    bad[1, 2] = 10_000       # far outside the pool
+    bad[0, 1] = -3
+    lens = torch.tensor([128, 128], dtype=torch.int32).cuda()
+    o = gqa.decode(q.cuda(), kp.cuda(), vp.cuda(), lens, block_table=bad.cuda(), page_size=page)
+    kz, vz = kc.clone(), vc.clone()
+    kz[1, :, 2 * page:3 * page] = 0
+    vz[1, :, 2 * page:3 * page] = 0
+    kz[0, :, page:2 * page] = 0
+    vz[0, :, page:2 * page] = 0
+    ref = gqa.decode(q.cuda(), kz.cuda(), vz.cuda(), lens)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all()
+    assert (o.float() - ref.float()).abs().max().item() <= 2e-2
