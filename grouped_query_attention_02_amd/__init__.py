@@ -17,8 +17,8 @@ from typing import Optional
 from ._lib import (GQA_DTYPE_BF16, GQA_DTYPE_F32, GQA_OK, GQAError, header_functions, load,
                    status_string)
 
-__all__ = ["prefill", "decode", "decode_workspace_bytes", "decode_num_workgroups", "version",
-           "status_string", "GQAError", "load", "header_functions"]
+__all__ = ["prefill", "decode", "decode_workspace_bytes", "decode_num_workgroups",
+           "mean_pool_heads", "version", "status_string", "GQAError", "load", "header_functions"]
 
 
 def version() -> int:
@@ -199,3 +199,24 @@ def decode(q, k_cache, v_cache, cache_lens=None, *, softmax_scale: Optional[floa
     if st != GQA_OK:
         raise GQAError(st, "gqa_decode_ex")
     return (out, lse_out) if return_lse else out
+
+
+def mean_pool_heads(w, num_groups: int, *, out=None):
+    """MHA -> GQA conversion: [H, ...] per-head weights (GPU, bfloat16 or float32,
+    contiguous) -> [num_groups, ...], each group the mean of its H/num_groups
+    consecutive heads."""
+    torch = _torch()
+    if not w.is_cuda or not w.is_contiguous():
+        raise ValueError("w must be a contiguous GPU tensor")
+    H = w.shape[0]
+    per_head = w.numel() // H if H else 0
+    if out is None:
+        out = torch.empty((num_groups,) + tuple(w.shape[1:]), dtype=w.dtype, device=w.device)
+    elif tuple(out.shape) != (num_groups,) + tuple(w.shape[1:]) or out.dtype != w.dtype \
+            or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [num_groups, ...] tensor of w's dtype")
+    st = load().gqa_mean_pool_heads(_dtype_code(w), w.data_ptr(), H, int(num_groups), per_head,
+                                    out.data_ptr(), _stream_ptr(w.device))
+    if st != GQA_OK:
+        raise GQAError(st, "gqa_mean_pool_heads")
+    return out

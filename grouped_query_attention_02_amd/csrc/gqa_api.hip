@@ -211,4 +211,18 @@ int gqa_decode(int dtype, const void* q, const void* k_cache, const void* v_cach
                        workspace_bytes, stream);
 }
 
+int gqa_mean_pool_heads(int dtype, const void* w, int H, int G, int64_t per_head, void* out,
+                        void* stream) {
+  if (!w || !out || H <= 0 || G <= 0 || H % G != 0 || per_head <= 0 || per_head % 8 != 0)
+    return GQA_ERR_INVALID_ARG;
+  if (!aligned16(w) || !aligned16(out)) return GQA_ERR_INVALID_ARG;
+  if (per_head / 8 > (int64_t)INT_MAX * 256 || G > 65535) return GQA_ERR_INVALID_ARG;
+  if (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16) return GQA_ERR_UNSUPPORTED;
+  gqa::MeanPoolParams p;
+  p.w = w; p.out = out; p.H = H; p.G = G; p.per_head = per_head;
+  hipError_t e =
+      gqa::launch_mean_pool(p, dtype == GQA_DTYPE_BF16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
 }  // extern "C"

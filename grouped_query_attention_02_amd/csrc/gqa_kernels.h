@@ -58,9 +58,18 @@ struct DecodeParams {
   int num_pages;              // pages in each of the K and V pools
 };
 
+// MHA -> GQA weight conversion: out[g] = mean of w[g * H/G .. (g + 1) * H/G - 1].
+struct MeanPoolParams {
+  const void* w;      // [H, per_head]
+  void* out;          // [G, per_head]
+  int H, G;
+  int64_t per_head;   // elements per head, a multiple of 8
+};
+
 hipError_t launch_prefill_bf16(const PrefillParams& p, int causal, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillParams& p, int causal, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeParams& p, bool need_combine, hipStream_t stream);
+hipError_t launch_mean_pool(const MeanPoolParams& p, bool bf16, hipStream_t stream);
 
 int prefill_rows_per_wg_bf16(int d);
 int prefill_rows_per_wg_f32();

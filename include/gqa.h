@@ -201,6 +201,27 @@ int gqa_decode_ex(int dtype, const void *q, const void *k_cache, const void *v_c
                   const float *alibi_slopes, int num_splits, void *workspace,
                   size_t workspace_bytes, void *stream);
 
+/*
+ * gqa_mean_pool_heads - convert per-head K or V projection weights of a
+ * multi-head checkpoint to G groups: each group's projection becomes the mean
+ * of its H/G consecutive heads (azimuth.plus GQA digest, "Idea 1", step 1, the
+ * conversion that is followed by a short continued pre-training).
+ *
+ *   dtype      GQA_DTYPE_BF16 or GQA_DTYPE_F32 (input and output); the sums
+ *              run in fp32, a bf16 output is rounded to nearest even.
+ *   w          [H, per_head] device array: head h's weights are the contiguous
+ *              per_head elements starting at h * per_head (for a projection
+ *              [H * d_head, d_model] that is per_head = d_head * d_model).
+ *   H, G       heads before and after; H % G == 0 (G = 1: MQA, G = H: copy).
+ *   per_head   elements per head, a positive multiple of 8.
+ *   out        [G, per_head] device array; must not overlap w.
+ *   stream     hipStream_t or NULL.
+ * Returns GQA_OK, GQA_ERR_INVALID_ARG (shapes, NULL or misaligned pointers),
+ * GQA_ERR_UNSUPPORTED (dtype) or GQA_ERR_HIP.
+ */
+int gqa_mean_pool_heads(int dtype, const void *w, int H, int G, int64_t per_head, void *out,
+                        void *stream);
+
 #ifdef __cplusplus
 }
 #endif

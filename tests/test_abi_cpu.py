@@ -159,3 +159,20 @@ def _decode_ex(lib, table=None, page=0, blocks=0, pages=0, window=0, slopes=None
 ])
 def test_decode_ex_rejects(lib, kw, code):
     assert _decode_ex(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=12, G=5), INV),
+    (dict(G=0), INV),
+    (dict(per_head=12), INV),           # not a multiple of 8
+    (dict(per_head=0), INV),
+    (dict(w=None), INV),
+    (dict(w=P + 4), INV),
+    (dict(out=P + 8), INV),
+    (dict(dtype=5), UNS),
+])
+def test_mean_pool_rejects(lib, kw, code):
+    a = dict(dtype=BF16, w=P, H=12, G=3, per_head=64, out=P)
+    a.update(kw)
+    assert lib.gqa_mean_pool_heads(a["dtype"], a["w"], a["H"], a["G"], a["per_head"], a["out"],
+                                   None) == code
