@@ -110,6 +110,76 @@ def _time_loop(fn, c, reps, warm, warm_s=1.0):
     return _ms(evs)
 
 
+def _alibi_slopes(H):
+    return [2.0 ** (-8.0 * (k + 1) / H) for k in range(H)]
+
+
+def _extended_rows(steps, dev):
+    """The optional paths, each timed on its full-size workload:
+    causal Llama-shaped prefill with a 1024-key sliding window and ALiBi; the MQA ragged
+    decode read from a paged cache (256-key pages scattered over the pool); and the
+    MHA -> GQA conversion of a Llama-2-70B-shaped K projection (64 -> 8 heads)."""
+    import numpy as np
+    import torch
+    import workloads as W
+    import grouped_query_attention_02_amd as gqa
+    from grouped_query_attention_02_amd import perfmodel
+    out = {}
+    reps = max(10, steps // 2)
+
+    lc = _prefill_case(W.WORKLOADS["llama_causal_prefill"], dev)
+    w, window, slopes = lc["w"], 1024, torch.tensor(_alibi_slopes(32), device=dev)
+    flops = perfmodel.prefill_flops(w.B, w.S, w.Hq, w.d, True, None, window)
+
+    def run_win(c):
+        gqa.prefill(c["q"], c["k"], c["v"], causal=True, softmax_scale=w.softmax_scale,
+                    window=window, alibi_slopes=slopes, out=c["out"])
+    ms = _time_loop(run_win, lc, reps, 3)
+    out["llama_causal_prefill_window1024_alibi"] = {
+        "tflops": flops / (statistics.mean(ms) * 1e-3) / 1e12,
+        "frac_mfma_peak": flops / (statistics.mean(ms) * 1e-3) / 1e12 / perfmodel.PEAK_BF16_TFLOPS,
+        "ms_mean": statistics.mean(ms), "flops": flops, "window": window}
+    del lc
+    torch.cuda.empty_cache()
+
+    dc = _decode_case(W.WORKLOADS["mqa_ragged_decode"], dev)
+    wd, page = dc["w"], 256
+    mb = wd.max_len // page
+    n_pages = wd.B * mb + 7
+    perm = np.random.default_rng(12).permutation(n_pages)
+    table = torch.tensor(perm[: wd.B * mb].reshape(wd.B, mb), dtype=torch.int32, device=dev)
+    def to_pool(c):
+        pool = torch.zeros((n_pages, wd.Hkv, page, wd.d), dtype=c.dtype, device=dev)
+        pool[table.view(-1).long()] = c.view(wd.B, wd.Hkv, mb, page, wd.d) \
+            .permute(0, 2, 1, 3, 4).reshape(wd.B * mb, wd.Hkv, page, wd.d)
+        return pool
+    dc["kp"], dc["vp"] = to_pool(dc["kc"]), to_pool(dc["vc"])
+    del dc["kc"], dc["vc"]
+
+    def run_paged(c):
+        gqa.decode(c["q"], c["kp"], c["vp"], c["lens"], softmax_scale=wd.softmax_scale,
+                   block_table=table, page_size=page, workspace=c["ws"], out=c["out"])
+    ms = _time_loop(run_paged, dc, reps, 3)
+    out["mqa_ragged_decode_paged256"] = {
+        "gbps": dc["bytes"] / (statistics.mean(ms) * 1e-3) / 1e9,
+        "frac_hbm_peak": dc["bytes"] / (statistics.mean(ms) * 1e-3) / 1e9 / perfmodel.PEAK_HBM_GBPS,
+        "ms_mean": statistics.mean(ms), "bytes": dc["bytes"], "page_size": page}
+    del dc
+    torch.cuda.empty_cache()
+
+    H, G, per_head = 64, 8, 128 * 8192
+    g = torch.Generator(device=dev).manual_seed(70)
+    wk = (torch.randn((H, per_head), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    pooled = torch.empty((G, per_head), dtype=torch.bfloat16, device=dev)
+    ms = _time_loop(lambda c: gqa.mean_pool_heads(wk, G, out=pooled), None, reps, 3)
+    nb = perfmodel.mean_pool_bytes(H, G, per_head, 2)
+    out["mean_pool_llama70b_kproj"] = {
+        "gbps": nb / (statistics.mean(ms) * 1e-3) / 1e9,
+        "frac_hbm_peak": nb / (statistics.mean(ms) * 1e-3) / 1e9 / perfmodel.PEAK_HBM_GBPS,
+        "ms_mean": statistics.mean(ms), "bytes": nb}
+    return out
+
+
 def _cpu_baseline(pc, target_s: float):
     """The fp64 oracle, as it stands, on a random row sample of the prefill workload."""
     import numpy as np
@@ -329,6 +399,7 @@ def main(argv=None):
         ms = _time_loop(_run_prefill, tc, 20, 3)
         also["tiny_f32_prefill"] = {"us_mean": statistics.mean(ms) * 1e3,
                                     "tflops": tc["flops"] / (statistics.mean(ms) * 1e-3) / 1e12}
+        also.update(_extended_rows(args.steps, dev))
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -230,10 +230,20 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_split_kernel(DecodeParam
         return (size_t)j0 * D;
       }
     };
+    // Every input of the descriptor is wave-uniform; reading each through readfirstlane
+    // tells the compiler so, which keeps every buffer load a single instruction (a
+    // descriptor it cannot prove uniform gets a loop over the distinct values per load).
     auto rsrc = [&](const uint16_t* base, int tt) {
       uint32_t valid;
       const size_t off = tile_src(tt, &valid);
-      return __builtin_amdgcn_make_buffer_rsrc((void*)(base + off), 0, valid, 0x00020000);
+      // (readfirstlane returns a signed int: go through uint32_t so that an address whose
+      // low word has bit 31 set is not sign-extended into the high word.)
+      const uint64_t a = reinterpret_cast<uint64_t>(base + off);
+      const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+      const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+      return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(lo | (hi << 32)), 0,
+                                               __builtin_amdgcn_readfirstlane(valid),
+                                               0x00020000);
     };
     auto load_k = [&](TileRegs& r, int tt) {
       const __amdgpu_buffer_rsrc_t rk = rsrc(kb_, tt);

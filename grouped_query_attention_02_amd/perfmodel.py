@@ -34,16 +34,21 @@ def kv_cache_reduction(h_q: int, groups: int) -> float:
     return h_q / groups
 
 
-def prefill_valid_pairs(B: int, S: int, causal: bool, seqlens: Optional[Sequence[int]]) -> int:
+def prefill_valid_pairs(B: int, S: int, causal: bool, seqlens: Optional[Sequence[int]],
+                        window: int = 0) -> int:
     """Valid (query row, key) pairs per head summed over the batch.
 
-    Key j is valid for query i iff j < L_b and (not causal or j <= i); every
-    query row i < S counts.
+    Key j is valid for query i iff j < L_b, (not causal or j <= i) and (window == 0 or
+    j > i - window); every query row i < S counts.
     """
     total = 0
     for b in range(B):
         L = S if seqlens is None else max(0, min(int(seqlens[b]), S))
-        if causal:
+        if window > 0:
+            for i in range(S):
+                hi = min(L, i + 1) if causal else L
+                total += max(0, hi - max(0, i - window + 1))
+        elif causal:
             # rows i < L see i + 1 keys; rows i >= L see L keys
             total += L * (L + 1) // 2 + (S - L) * L
         else:
@@ -52,15 +57,24 @@ def prefill_valid_pairs(B: int, S: int, causal: bool, seqlens: Optional[Sequence
 
 
 def prefill_flops(B: int, S: int, Hq: int, d: int, causal: bool,
-                  seqlens: Optional[Sequence[int]]) -> int:
-    return 4 * d * Hq * prefill_valid_pairs(B, S, causal, seqlens)
+                  seqlens: Optional[Sequence[int]], window: int = 0) -> int:
+    return 4 * d * Hq * prefill_valid_pairs(B, S, causal, seqlens, window)
 
 
 def decode_bytes(B: int, Hq: int, Hkv: int, d: int, lens: Sequence[int], max_len: int,
-                 esize: int) -> int:
-    total_len = sum(max(0, min(int(x), max_len)) for x in lens)
+                 esize: int, window: int = 0) -> int:
+    """Valid K/V rows read (the last `window` of each sequence when window > 0) plus q and o."""
+    def keys(x):
+        L = max(0, min(int(x), max_len))
+        return min(L, window) if window > 0 else L
+    total_len = sum(keys(x) for x in lens)
     cache = kv_cache_bytes(1, Hkv, d, total_len, esize)
     return cache + 2 * B * Hq * d * esize
+
+
+def mean_pool_bytes(H: int, G: int, per_head: int, esize: int) -> int:
+    """MHA -> GQA conversion traffic: every input element read once, every output written once."""
+    return (H + G) * per_head * esize
 
 
 def decode_flops(Hq: int, d: int, lens: Sequence[int], max_len: int) -> int:
