@@ -437,14 +437,14 @@ def main(argv=None):
             "peak": perfmodel.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(p_tflops / perfmodel.PEAK_BF16_TFLOPS, 4),
             "traffic": _recorded_traffic("prefill_bert_base_traffic.md", "prefill_bf16.hip"),
-            "kernel": "prefill_bf16_kernel<64, false>",
+            "kernel": "prefill_bf16_kernel<64, false, false, false>",
             "launch_us_mean": round(p_avg * 1e3, 2), "flops_per_launch": pc["flops"],
         },
         "decode": {
             "gbps": round(d_gbps, 2), "frac_hbm_peak": round(d_gbps / perfmodel.PEAK_HBM_GBPS, 4),
             "peak_gbps": perfmodel.PEAK_HBM_GBPS, "call_us_mean": round(d_avg * 1e3, 2),
             "call_us_min": round(min(d_ms) * 1e3, 2), "bytes_per_call": dc["bytes"],
-            "kernels": "decode_split_kernel<128> + decode_combine_kernel<128>",
+            "kernels": "decode_split_kernel<128, false, false> + decode_combine_kernel<128>",
         },
         "cpu_baseline": cpu,
         "also": also,
