@@ -19,7 +19,7 @@ struct PrefillParams {
   int B, S, Hq, Hkv, g, d;
   float scale_log2;   // |softmax_scale| * log2(e)
   float scale_abs;    // |softmax_scale|
-  int negate_q;       // 1 when softmax_scale < 0 (q is negated on load instead)
+  int negate_q;       // 1 when softmax_scale < 0 (the kernel negates q or the scores)
   int rows_per_wg;    // flattened rows per workgroup
   int nrb;            // row blocks per (b, kvh) unit
   int n_wg;           // B * Hkv * nrb

@@ -18,11 +18,11 @@
 //                        accumulators)
 // on v_mfma_f32_32x32x16_bf16. The kernel is kept small (at most 128 VGPRs for d <= 64)
 // so that several waves share each SIMD and the hardware overlaps one wave's matrix
-// products with another wave's softmax. K/V tiles stream from HBM/L2 straight into a
-// 4-slot LDS ring, three tiles ahead of their use. The running max used as the
-// exponent offset is refreshed only when a row's max grows by more than 2^8 (in exp2
-// units), so the O rescale is rare; every term of a row always shares one offset, so
-// the normalised result is unchanged. The result equals textbook softmax(scale Q K^T) V
+// products with another wave's softmax. K/V tiles stream from HBM/L2 straight into an
+// 4-slot LDS ring, three tiles ahead of their use. The exponent offset is a row
+// max that is raised only when a tile's weights would exceed 2^32, so the O rescale is
+// rare; every term of a row always shares one offset, so the normalised result is
+// unchanged. The result equals textbook softmax(scale Q K^T) V
 // over the valid keys (aifullclass.xyz BERT self-attention article, LowRankSelfAttention
 // example; FlashAttention page FAQ: the computed result is mathematically the same).
 //
@@ -35,8 +35,6 @@
 namespace gqa {
 namespace {
 
-constexpr int kRing = 4;      // LDS slots per K and per V ring
-constexpr int kAhead = 3;     // tiles in flight ahead of the one being read
 constexpr float kSumCap = 4294967296.0f;  // 2^32: a tile's weights stay at most this large
 
 // Waves per workgroup and workgroups per CU for head size D.
@@ -45,10 +43,21 @@ struct PfShape {
   // Keys per K/V tile: 64 while the registers allow four waves per SIMD, 32 for d = 128.
   static constexpr int BN = D == 128 ? 32 : 64;
   static constexpr int WAVES = D == 128 ? 4 : 8;
-  static constexpr int WG_PER_CU = D == 128 ? 3 : 2;
+  static constexpr int WG_PER_CU = 2;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int ROWS = 32 * WAVES;
   static constexpr int WAVES_PER_SIMD = WG_PER_CU * WAVES / 4;  // register budget 512 / this
+  // LDS slots per K and per V ring, and tiles in flight ahead of the one being read.
+  // (The 64 KB ring lets two workgroups share a CU; a 3-slot ring measured slower.)
+  static constexpr int RING = 4;
+  static constexpr int AHEAD = RING - 1;
+  // Persistent launch: one resident workgroup per slot works through a share of its XCD's
+  // queue. Used for d = 128 (one wave per SIMD per workgroup), where the two workgroups
+  // of a CU progress at the same rate. With two waves per SIMD per workgroup (d <= 64) the
+  // older workgroup of a CU takes most issue slots and a static share leaves the younger
+  // one finishing alone, so there every item gets its own workgroup and the hardware
+  // dispatcher balances the queue.
+  static constexpr bool PERSISTENT = D == 128;
 };
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
@@ -64,7 +73,7 @@ struct PfLayout {
   static constexpr int ROWB = D * 2;             // bytes per K or V row
   static constexpr int TILE_B = BN * ROWB;       // bytes per K or V tile
   static constexpr int NWI = BN * CPR / 64;      // 1 KB DMA wave-instructions per tile
-  static constexpr int LDS_BYTES = 2 * kRing * TILE_B;
+  static constexpr int LDS_BYTES = 2 * PfShape<D>::RING * TILE_B;
   // Tiles are stored unpadded (DMA writes 1 KB contiguous per wave instruction); the
   // 16-byte chunk q of row r sits at chunk position q ^ f(r). fk makes the K fragment
   // reads (16 rows x one chunk per pass) hit 16 different bank groups; fv does the same
@@ -124,7 +133,8 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
   constexpr int NKB = Lay::NKB, NKS = Lay::NKS;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
-  // LDS: K slots 0..kRing-1, then V slots 0..kRing-1 (byte offsets).
+  // LDS: K slots 0..RING-1, then V slots 0..RING-1 (byte offsets).
+  constexpr int kRing = Shp::RING, kAhead = Shp::AHEAD;
   auto kslot = [](int t) { return (t % kRing) * Lay::TILE_B; };
   auto vslot = [](int t) { return (kRing + t % kRing) * Lay::TILE_B; };
 
@@ -134,31 +144,29 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  // Launch index -> work. Workgroups are dealt round-robin to the 8 XCDs (launch index
-  // lin runs on XCD lin % 8, in increasing lin / 8); all row blocks of one (b, kvh) unit,
-  // which share K/V, go to the same XCD so the unit's K/V stays in that XCD's L2.
+  // ---- Work list. The (b, kvh, row block) items are dealt to 8 XCD queues (launch index
+  // lin runs on XCD lin % 8); all row blocks of one (b, kvh) unit, which share K/V, sit in
+  // one queue so the unit's K/V stays in that XCD's L2. The grid holds P = gridDim.x / 8
+  // resident workgroups per XCD; slot s of an XCD takes queue positions s, 2P-1-s, 2P+s,
+  // 4P-1-s, ... (snake order), so with each queue ordered heaviest first every slot gets
+  // about the same amount of work. A workgroup streams the K/V tiles of all its items
+  // through one LDS ring: the next item's first tiles are in flight while the current item
+  // finishes, and no workgroup start-up or tail is paid per item.
   const int g = p.g, S = p.S, Hq = p.Hq, Hkv = p.Hkv;
+  const int R = S * g;
   const int lin = blockIdx.x;
-  const int xcd = lin & 7, qpos = lin >> 3;
-  int b, kvh, rb, Lb = S;
+  const int xcd = lin & 7, slot = lin >> 3, P = gridDim.x >> 3;
+  int* s_len = reinterpret_cast<int*>(smem + Lay::LDS_BYTES);  // [B] clamped L_b
+  int* s_order = s_len + kPrefillLptMaxB;                       // [rank] -> sequence
   if (p.lpt) {
-    // Ragged batch: sort the sequences by length (longest first, ties by index) and deal
-    // the units of that order to the XCD queues in snake order 0..7, 7..0, ..., so every
-    // XCD gets about the same number of key tiles and each queue runs its longest units
-    // first. The lengths are staged in the (not yet used) K/V ring.
-    int* s_len = reinterpret_cast<int*>(smem);
-    int* s_sel = s_len + kPrefillLptMaxB;
+    // Ragged batch: sort the sequences by length (longest first, ties by index); the
+    // units of that order are dealt to the XCD queues in snake order 0..7, 7..0, ..., so
+    // every queue gets about the same number of key tiles, longest units first.
     for (int i = tid; i < p.B; i += Shp::THREADS) {
       const int L = p.seqlens[i];
       s_len[i] = L < 0 ? 0 : (L > S ? S : L);
     }
     __syncthreads();
-    const int upos = qpos / p.nrb;                          // unit slot in this queue
-    const int r = 8 * upos + ((upos & 1) ? 7 - xcd : xcd);  // rank of the unit
-    if (r >= p.B * Hkv) return;                             // uniform per workgroup
-    const int rank_b = r / Hkv;                             // rank of the sequence
-    kvh = r - rank_b * Hkv;
-    rb = qpos - upos * p.nrb;
     for (int i = tid; i < p.B; i += Shp::THREADS) {
       const int Li = s_len[i];
       int rank = 0;
@@ -166,78 +174,61 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
         const int Lj = s_len[j];
         rank += (Lj > Li) | ((Lj == Li) & (j < i));
       }
-      if (rank == rank_b) *s_sel = i;
+      s_order[rank] = i;
     }
     __syncthreads();
-    b = *s_sel;
-    Lb = s_len[b];
-    __syncthreads();  // the ring is written by the first copies below
-  } else {
-    // Each XCD takes a contiguous range of logical blocks.
-    const int logical = xcd * p.per_xcd + qpos;
-    if (logical >= p.n_wg) return;
-    const int unit = logical / p.nrb;
-    rb = logical - unit * p.nrb;
-    b = unit / Hkv;
-    kvh = unit - b * Hkv;
-    if (p.seqlens) {
-      Lb = p.seqlens[b];
-      Lb = Lb < 0 ? 0 : (Lb > S ? S : Lb);
+  }
+  // Sequence lengths read with a uniform index go through the scalar cache (the array
+  // does not change during the kernel), so they never wait on the vector-memory counter.
+  const __attribute__((address_space(4))) int* seqlens_k =
+      (const __attribute__((address_space(4))) int*)p.seqlens;
+  struct Item {
+    int b, kvh, rb, Lb;
+  };
+  // Item k of this workgroup; false past the end of its share (positions grow with k).
+  auto get_item = [&](int k, Item& it) -> bool {
+    const int qpos = (k & 1) ? (k + 1) * P - 1 - slot : k * P + slot;
+    if (qpos >= p.per_xcd) return false;
+    if (p.lpt) {
+      const int upos = qpos / p.nrb;                          // unit slot in this queue
+      const int r = 8 * upos + ((upos & 1) ? 7 - xcd : xcd);  // rank of the unit
+      if (r >= p.B * Hkv) return false;
+      const int rank_b = r / Hkv;
+      it.kvh = r - rank_b * Hkv;
+      it.rb = qpos - upos * p.nrb;
+      it.b = __builtin_amdgcn_readfirstlane(s_order[rank_b]);
+      it.Lb = __builtin_amdgcn_readfirstlane(s_len[it.b]);
+    } else {
+      const int logical = xcd * p.per_xcd + qpos;  // each XCD: a contiguous range
+      if (logical >= p.n_wg) return false;
+      const int unit = logical / p.nrb;
+      it.rb = logical - unit * p.nrb;
+      it.b = unit / Hkv;
+      it.kvh = unit - it.b * Hkv;
+      it.Lb = S;
+      if (p.seqlens) {
+        const int L = seqlens_k[it.b];
+        it.Lb = L < 0 ? 0 : (L > S ? S : L);
+      }
     }
-  }
-  if (CAUSAL) rb = p.nrb - 1 - rb;  // heaviest row blocks first
-  const int R = S * g;
-  const int f0 = rb * ROWS;
-  const int fw = f0 + wave * 32;
-  const int f = fw + l32;
-  const bool row_ok = f < R;
-  const int qi = row_ok ? f / g : 0;
-  const int hq = kvh * g + (row_ok ? f - qi * g : 0);
-
-  int kv_end = Lb;                 // keys the workgroup visits
-  int wave_kv_end = kv_end;        // keys this wave needs
-  int wave_mask_from = Lb;         // first key at which some row of the wave is masked
-  if (CAUSAL) {
-    const int last_f = min(f0 + ROWS, R) - 1;
-    kv_end = min(Lb, last_f / g + 1);
-    const int wf_last = min(fw + 31, R - 1);
-    wave_kv_end = (fw < R) ? min(Lb, wf_last / g + 1) : 0;
-    wave_mask_from = min(Lb, fw / g + 1);
-  }
-  const int lim = CAUSAL ? min(Lb, qi + 1) : Lb;  // keys j < lim are visible to this row
-  const int ntiles = (kv_end + PF_BN - 1) / PF_BN;
-  const int wave_nt = (wave_kv_end + PF_BN - 1) / PF_BN;
-  // Sliding window: key j is also required to satisfy j >= lo = i - window + 1. Tiles
-  // below the lowest row's bound are skipped (the workgroup's and each wave's own).
-  constexpr int kNoLo = -(1 << 30);
-  int lo = kNoLo, t_first = 0, wave_t0 = 0, wave_lo_hi = kNoLo;
-  if constexpr (WINDOW) {
-    lo = qi - p.window + 1;
-    t_first = max(0, f0 / g - p.window + 1) / PF_BN;
-    if (fw < R) {
-      wave_t0 = max(0, fw / g - p.window + 1) / PF_BN;
-      wave_lo_hi = min(fw + 31, R - 1) / g - p.window + 1;  // highest bound in the wave
-    }
-  }
-
-  // Q^T as the B operand: lane holds query row f, d = ks*16 + hh*8 .. +7.
-  bf16x8 qf[D / 16];
-  {
-    const uint16_t* qrow =
-        static_cast<const uint16_t*>(p.q) + (((size_t)b * S + qi) * Hq + hq) * D;
-    const uint32_t flip = p.negate_q ? 0x80008000u : 0u;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      u32x4 v = row_ok ? ldg16(qrow + ks * 16 + hh * 8) : zero_u32x4();
-      v[0] ^= flip; v[1] ^= flip; v[2] ^= flip; v[3] ^= flip;
-      qf[ks] = as_bf16x8(v);
-    }
-  }
+    if (CAUSAL) it.rb = p.nrb - 1 - it.rb;  // heaviest row blocks first
+    return true;
+  };
+  // Key tiles [t_first, ntiles) that the workgroup visits for an item. With a sliding
+  // window, key j must also satisfy j >= i - window + 1: tiles below the lowest row's
+  // bound are skipped.
+  auto item_tiles = [&](const Item& it, int& t_first, int& ntiles) {
+    const int f0 = it.rb * ROWS;
+    int kv_end = it.Lb;
+    if (CAUSAL) kv_end = min(it.Lb, (min(f0 + ROWS, R) - 1) / g + 1);
+    ntiles = (kv_end + PF_BN - 1) / PF_BN;
+    t_first = WINDOW ? max(0, f0 / g - p.window + 1) / PF_BN : 0;
+  };
 
   const size_t rstride = (size_t)Hkv * D;  // elements between consecutive keys (BSHD)
-  const uint16_t* kbase = static_cast<const uint16_t*>(p.k) + ((size_t)b * S * Hkv + kvh) * D;
-  const uint16_t* vbase = static_cast<const uint16_t*>(p.v) + ((size_t)b * S * Hkv + kvh) * D;
   const uint32_t row_bytes = (uint32_t)(rstride * 2);
+  const uint16_t* const k_all = static_cast<const uint16_t*>(p.k);
+  const uint16_t* const v_all = static_cast<const uint16_t*>(p.v);
 
   // ---- DMA of one K/V tile pair. Wave-instruction k (of 2 * NWI per tile pair) is taken
   // by wave k % WAVES; k < NWI copies K chunk block k, otherwise V chunk block k - NWI.
@@ -260,43 +251,62 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
     const int q = pos ^ (is_k ? Lay::fk(row) : Lay::fv(row));
     voff[j] = (uint32_t)row * row_bytes + 16u * q;
   }
-  auto issue_tile = [&](int t) {
-    const int t0 = t * PF_BN;
-    const uint32_t valid = (uint32_t)max(Lb - t0, 0) * row_bytes;
-    const i32x4 rk = make_rsrc(kbase + (size_t)t0 * rstride, valid);
-    const i32x4 rv = make_rsrc(vbase + (size_t)t0 * rstride, valid);
+  // Issue cursor: the next tile to copy is tile it_t of item it_k (tiles up to it_end);
+  // it_kp / it_vp point at the item's K and V rows, it_L is its length.
+  int it_k = -1, it_t = 0, it_end = 0, it_L = 0;
+  bool live = true;
+  const uint16_t* it_kp = k_all;
+  const uint16_t* it_vp = v_all;
+  auto seek = [&]() {  // move the cursor to the next item that has tiles
+    for (;;) {
+      Item n;
+      if (!get_item(++it_k, n)) {
+        live = false;
+        it_t = 0;
+        it_L = 0;
+        return;
+      }
+      int t0, nt;
+      item_tiles(n, t0, nt);
+      if (t0 < nt) {
+        it_t = t0;
+        it_end = nt;
+        it_L = n.Lb;
+        it_kp = k_all + ((size_t)n.b * S * Hkv + n.kvh) * D;
+        it_vp = v_all + ((size_t)n.b * S * Hkv + n.kvh) * D;
+        return;
+      }
+    }
+  };
+  // Copy the cursor's tile into ring position u and advance. Past the last item the copy
+  // has an empty resource and zeros land in the (free) slot: every wave issues the same
+  // number of copies per ring position, which keeps the waits below exact.
+  auto issue = [&](int u) {
+    const int t0 = it_t * PF_BN;
+    const uint32_t valid = (uint32_t)max(it_L - t0, 0) * row_bytes;
+    const i32x4 rk = make_rsrc(it_kp + (size_t)t0 * rstride, valid);
+    const i32x4 rv = make_rsrc(it_vp + (size_t)t0 * rstride, valid);
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {
       const int k = kidx[j];
       if (k < Lay::NWI)
-        dma16(rk, voff[j], lds_base + kslot(t) + k * 1024);
+        dma16(rk, voff[j], lds_base + kslot(u) + k * 1024);
       else
-        dma16(rv, voff[j], lds_base + vslot(t) + (k - Lay::NWI) * 1024);
+        dma16(rv, voff[j], lds_base + vslot(u) + (k - Lay::NWI) * 1024);
+    }
+    if (live && ++it_t == it_end) {
+      if constexpr (Shp::PERSISTENT)
+        seek();
+      else
+        live = false, it_L = 0;  // one item per workgroup
     }
   };
 
-  // ---- per-tile math
-  f32x16 oacc[D / 32];
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i) oacc[i] = zero16();
-
+  // ---- per-lane constants of the fragment layouts
   // S^T = K Q^T for a 32-key block: lane holds query l32, keys 8(r/4)+4hh+(r%4).
   // Chunk (2ks + hh) of row l32 sits at position (2ks + hh) ^ fk(l32).
   const int k_lane = l32 * Lay::ROWB + 16 * (hh ^ (Lay::fk(l32) & 1));
   const int k_swz = Lay::fk(l32) & ~1;
-  auto qk = [&](f32x16 (&s)[NKB], int slot_off) {
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) s[kb] = zero16();
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(smem + slot_off + kb * 32 * Lay::ROWB +
-                                                        k_lane + 16 * ((2 * ks) ^ k_swz));
-        s[kb] = mfma_bf16_32x32x16(as_bf16x8(a), qf[ks], s[kb]);
-      }
-    }
-  };
   // O^T += V^T P^T, 16 keys per MFMA; B slot i <-> key 16ks + 8(i/4) + 4hh + (i%4).
   // The transposing read hands lane (group G = lane/16, i = lane%16) keys
   // 16ks + 4(G/2) + {0..3} (and +8) of output column d = db*32 + (lane % 32): lane i of a
@@ -305,195 +315,300 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
   const int tr_q = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // chunk within the 32 columns
   const int v_lane = tr_row * Lay::ROWB + 8 * (lane & 1);
   const int v_swz = Lay::fv(tr_row);  // the same for every (ks, db, +8 rows)
-  auto pv = [&](const bf16x8 (&pp)[NKS], int slot_off) {
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const int off = slot_off + ks * 16 * Lay::ROWB + v_lane + 16 * ((4 * db + tr_q) ^ v_swz);
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(smem + off));
-        const s16x4 hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(smem + off + 8 * Lay::ROWB));
-        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-        const u32x4 a = {l2[0], l2[1], h2[0], h2[1]};
-        oacc[db] = mfma_bf16_32x32x16(as_bf16x8(a), pp[ks], oacc[db]);
-      }
-    }
-  };
-
-  // ---- online softmax state (one query row per lane; lanes l and l^32 share a row)
-  // With a window, m_run stays -inf until the row sees a key; otherwise key 0 is visible to
-  // every row and the first tile always sets it.
-  float m_run = WINDOW ? -INFINITY : 0.f, l_run = 0.f;
   const float c = p.scale_log2;
-  // ALiBi: the score gets -slope_h * |i - j|, i.e. -beta * |i - j| in the units of the raw
-  // dot product that c = |scale| * log2(e) scales into exp2 units.
-  float beta = 0.f;
-  if constexpr (ALIBI) beta = p.alibi[hq] * kLog2e / c;
-
-  // Key j = t0 + 32kb + 8(r/4) + 4hh + (r%4) is kept iff lo <= j < lim: the signs of
-  // j - lim and j - lo select between the score and -inf bit patterns (no compare masks
-  // in SGPRs).
-  auto mask = [&](f32x16 (&s)[NKB], int t0) {
-    const int base = t0 + 4 * hh - lim;
-    const int base_lo = t0 + 4 * hh - lo;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int jj = 32 * kb + 8 * (r >> 2) + (r & 3);
-        uint32_t keep = (uint32_t)((base + jj) >> 31);
-        if constexpr (WINDOW) keep &= ~(uint32_t)((base_lo + jj) >> 31);
-        s[kb][r] = __uint_as_float((__float_as_uint(s[kb][r]) & keep) | (0xff800000u & ~keep));
-      }
-  };
-  // Mask tile t's scores if any key of the wave's rows is masked in it.
-  auto prep = [&](f32x16 (&s)[NKB], int t) {
-    const int t0 = t * PF_BN;
-    if (t0 + PF_BN > wave_mask_from || (WINDOW && t0 < wave_lo_hi)) mask(s, t0);
-  };
-  // ALiBi distance |i - j| of this lane's score (kb, r) in tile t: key j = t0 + 32kb +
-  // 8(r/4) + 4hh + (r%4), so i - j = dq(t) - (32kb + 8(r/4) + r%4).
-  // (The empty asm hides where dq came from, so the compiler recomputes the distances in
-  // each use instead of keeping 32 of them live between the row max and the weights.)
-  auto alibi_dq = [&](int t) {
-    float dq = (float)(qi - t * PF_BN - 4 * hh);
-    asm volatile("" : "+v"(dq));
-    return dq;
-  };
-  auto alibi_off = [](int kb, int r) { return (float)(32 * kb + 8 * (r >> 2) + (r & 3)); };
-  // Row max of the (biased) scores over the tile (the row's other keys sit in lane l ^ 32).
-  auto row_max = [&](const f32x16 (&s)[NKB], int t) {
-    float mx = -INFINITY;
-    const float dq = ALIBI ? alibi_dq(t) : 0.f;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[kb][r];
-        if constexpr (ALIBI) x = fmaf(-beta, fabsf(dq - alibi_off(kb, r)), x);
-        mx = fmaxf(mx, x);
-      }
-    return pair_max(mx);
-  };
-  // Weights exp2(c s - c m) rounded to bf16 as the PV operand; returns this lane's sum of
-  // the rounded weights (the same values the PV product uses). exp2(-inf) = 0.
   const bf16x2 ones2 = __builtin_bit_cast(bf16x2, 0x3f803f80u);
-  auto weights = [&](const f32x16 (&s)[NKB], bf16x8 (&pp)[NKS], int t) {
-    const float msc = ((WINDOW && m_run == -INFINITY) ? 0.f : m_run) * c;  // no key yet
-    const float dq = ALIBI ? alibi_dq(t) : 0.f;
-    const float bc = beta * c;  // the bias slope in exp2 units
-    // exp2 argument of score (kb, r): c * (s - beta |i - j|) - c * m
-    auto arg = [&](int kb, int r) {
-      float x = fmaf(s[kb][r], c, -msc);
-      if constexpr (ALIBI) x = fmaf(-bc, fabsf(dq - alibi_off(kb, r)), x);
-      return x;
-    };
-    float lsum = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      u32x4 u;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kb = ks >> 1, r0 = 8 * (ks & 1) + 2 * i;
-        const f32x2 e = {fast_exp2(arg(kb, r0)), fast_exp2(arg(kb, r0 + 1))};
-        const bf16x2 h = __builtin_convertvector(e, bf16x2);
-        u[i] = __builtin_bit_cast(uint32_t, h);
-        // The dot operand is the converted pair itself: bit-casting it back out of u[i]
-        // makes this compiler feed the same register to every dot instruction.
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(h, ones2, lsum, false);
-      }
-      pp[ks] = as_bf16x8(u);
-    }
-    return lsum;
-  };
+  // A negative softmax scale: the kernel works with the negated scores -q.k (and |scale|),
+  // so masked scores are +inf before the sign is applied.
+  const float sgn = p.negate_q ? -1.f : 1.f;
+  const float cs = c * sgn;
+  const uint32_t masked_bits = p.negate_q ? 0x7f800000u : 0xff800000u;
 
-  // The exponent offset m_run is the row max of the first tile in which the row sees a
-  // key, and stays fixed while every weight of a tile is at most 2^32 (checked through the
-  // tile's weight sum, which bounds each weight). A tile that breaks this (scores grown
-  // past the offset) is redone with the offset raised to its row max, after rescaling what
-  // was accumulated. Every term of a row always shares one offset, so the normalised
-  // result is that of the exact max.
-  auto tile = [&](int t) {
-    f32x16 s[NKB];
-    qk(s, kslot(t));
-    prep(s, t);
-    if constexpr (WINDOW) {
-      if (wave_any(m_run == -INFINITY)) {  // rows that have not seen a key yet
-        const float mx = row_max(s, t);
-        if (m_run == -INFINITY) m_run = mx;  // stays -inf while all the row's keys are masked
-      }
-    } else if (t == 0) {
-      m_run = row_max(s, t);  // key 0 is visible to every row, so this is finite
+  Item cur;
+  if (!get_item(0, cur)) return;  // uniform: no work for this workgroup
+  seek();
+  // ---- pipeline: the copy of ring position u + kAhead is issued while position u is
+  // computed (after its scores are read, so a wait for Q never covers it); after position
+  // u each wave waits for its own copies of u + 1 and the barrier publishes everyone's.
+  // The first copies are issued after the first item's Q loads, so the two overlap.
+  int u = 0;
+
+  for (int item_no = 0;; ++item_no) {
+    if (item_no > 0 && (!Shp::PERSISTENT || !get_item(item_no, cur))) break;
+    const int b = cur.b, kvh = cur.kvh, Lb = cur.Lb;
+    const int f0 = cur.rb * ROWS;
+    const int fw = f0 + wave * 32;
+    const int f = fw + l32;
+    const bool row_ok = f < R;
+    const int qi = row_ok ? f / g : 0;  // rows past the end compute row 0, never stored
+    const int hq = kvh * g + (row_ok ? f - qi * g : 0);
+
+    int wave_kv_end = Lb;     // keys this wave needs
+    int wave_mask_from = Lb;  // first key at which some row of the wave is masked
+    if (CAUSAL) {
+      const int wf_last = min(fw + 31, R - 1);
+      wave_kv_end = (fw < R) ? min(Lb, wf_last / g + 1) : 0;
+      wave_mask_from = min(Lb, fw / g + 1);
     }
-    bf16x8 pp[NKS];
-    float lsum = weights(s, pp, t);
-    if (wave_any(!(lsum <= kSumCap))) {
-      // Recompute the scores from the K tile (still in LDS) rather than keeping them live
-      // through the common path: the empty asm keeps the compiler from reusing them.
-      asm volatile("" ::: "memory");
-      qk(s, kslot(t));
+    const int lim = CAUSAL ? min(Lb, qi + 1) : Lb;  // keys j < lim are visible to this row
+    int t_first, ntiles;
+    item_tiles(cur, t_first, ntiles);
+    const int wave_nt = (wave_kv_end + PF_BN - 1) / PF_BN;
+    constexpr int kNoLo = -(1 << 30);
+    int lo = kNoLo, wave_t0 = 0, wave_lo_hi = kNoLo;
+    if constexpr (WINDOW) {
+      lo = qi - p.window + 1;
+      if (fw < R) {
+        wave_t0 = max(0, fw / g - p.window + 1) / PF_BN;
+        wave_lo_hi = min(fw + 31, R - 1) / g - p.window + 1;  // highest bound in the wave
+      }
+    }
+
+    // Q^T as the B operand: lane holds query row f, d = ks*16 + hh*8 .. +7.
+    bf16x8 qf[D / 16];
+    {
+      const uint16_t* qrow =
+          static_cast<const uint16_t*>(p.q) + (((size_t)b * S + qi) * Hq + hq) * D;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) qf[ks] = as_bf16x8(ldg16(qrow + ks * 16 + hh * 8));
+    }
+    if (item_no == 0) {
+#pragma unroll
+      for (int a = 0; a < kAhead; ++a) issue(a);
+      wait_vm<kJ * (kAhead - 1)>();  // position 0 has landed
+      block_barrier();
+    }
+    // Take the compiler's wait for the Q loads here, once per item: its first real use is
+    // inside the tile loop, where the wait would otherwise be repeated on every tile (and,
+    // not knowing about the copies, it waits for all of them).
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) asm volatile("" ::"v"(qf[ks]));
+
+    f32x16 oacc[D / 32];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) oacc[i] = zero16();
+
+    auto qk = [&](f32x16 (&s)[NKB], int slot_off) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) s[kb] = zero16();
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(smem + slot_off + kb * 32 * Lay::ROWB +
+                                                          k_lane + 16 * ((2 * ks) ^ k_swz));
+          s[kb] = mfma_bf16_32x32x16(as_bf16x8(a), qf[ks], s[kb]);
+        }
+      }
+    };
+    auto pv = [&](const bf16x8 (&pp)[NKS], int slot_off) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const int off = slot_off + ks * 16 * Lay::ROWB + v_lane + 16 * ((4 * db + tr_q) ^ v_swz);
+          const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(smem + off));
+          const s16x4 hi4 =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(smem + off + 8 * Lay::ROWB));
+          const u32x2 l2 = __builtin_bit_cast(u32x2, lo4), h2 = __builtin_bit_cast(u32x2, hi4);
+          const u32x4 a = {l2[0], l2[1], h2[0], h2[1]};
+          oacc[db] = mfma_bf16_32x32x16(as_bf16x8(a), pp[ks], oacc[db]);
+        }
+      }
+    };
+
+    // ---- online softmax state (one query row per lane; lanes l and l^32 share a row)
+    // With a window, m_run stays -inf until the row sees a key; otherwise key 0 is visible
+    // to every row and the first tile always sets it.
+    float m_run = WINDOW ? -INFINITY : 0.f, l_run = 0.f;
+    // ALiBi: the score gets -slope_h * |i - j|, i.e. -beta * |i - j| in the units of the
+    // raw dot product that c = |scale| * log2(e) scales into exp2 units.
+    float beta = 0.f;
+    if constexpr (ALIBI) beta = p.alibi[hq] * kLog2e / c;
+
+    // Key j = t0 + 32kb + 8(r/4) + 4hh + (r%4) is kept iff lo <= j < lim: the signs of
+    // j - lim and j - lo select between the score and -inf bit patterns (no compare masks
+    // in SGPRs).
+    auto mask = [&](f32x16 (&s)[NKB], int t0) {
+      const int base = t0 + 4 * hh - lim;
+      const int base_lo = t0 + 4 * hh - lo;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int jj = 32 * kb + 8 * (r >> 2) + (r & 3);
+          uint32_t keep = (uint32_t)((base + jj) >> 31);
+          if constexpr (WINDOW) keep &= ~(uint32_t)((base_lo + jj) >> 31);
+          s[kb][r] = __uint_as_float((__float_as_uint(s[kb][r]) & keep) | (masked_bits & ~keep));
+        }
+    };
+    // Mask tile t's scores if any key of the wave's rows is masked in it.
+    auto prep = [&](f32x16 (&s)[NKB], int t) {
+      const int t0 = t * PF_BN;
+      if (t0 + PF_BN > wave_mask_from || (WINDOW && t0 < wave_lo_hi)) mask(s, t0);
+    };
+    // ALiBi distance |i - j| of this lane's score (kb, r) in tile t: key j = t0 + 32kb +
+    // 8(r/4) + 4hh + (r%4), so i - j = dq(t) - (32kb + 8(r/4) + r%4).
+    // (The empty asm hides where dq came from, so the compiler recomputes the distances in
+    // each use instead of keeping 32 of them live between the row max and the weights.)
+    auto alibi_dq = [&](int t) {
+      float dq = (float)(qi - t * PF_BN - 4 * hh);
+      asm volatile("" : "+v"(dq));
+      return dq;
+    };
+    auto alibi_off = [](int kb, int r) { return (float)(32 * kb + 8 * (r >> 2) + (r & 3)); };
+    // Row max of the (signed, biased) scores over the tile (the row's other keys sit in lane
+    // l ^ 32).
+    auto row_max = [&](const f32x16 (&s)[NKB], int t) {
+      float mx = -INFINITY;
+      const float dq = ALIBI ? alibi_dq(t) : 0.f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = s[kb][r] * sgn;
+          if constexpr (ALIBI) x = fmaf(-beta, fabsf(dq - alibi_off(kb, r)), x);
+          mx = fmaxf(mx, x);
+        }
+      return pair_max(mx);
+    };
+    // Weights exp2(c sgn s - c m) rounded to bf16 as the PV operand; returns this lane's sum
+    // of the rounded weights (the same values the PV product uses). exp2(-inf) = 0.
+    auto weights = [&](const f32x16 (&s)[NKB], bf16x8 (&pp)[NKS], int t) {
+      const float msc = ((WINDOW && m_run == -INFINITY) ? 0.f : m_run) * c;  // no key yet
+      const float dq = ALIBI ? alibi_dq(t) : 0.f;
+      const float bc = beta * c;  // the bias slope in exp2 units
+      // exp2 argument of score (kb, r): c * (sgn s - beta |i - j|) - c * m
+      auto arg = [&](int kb, int r) {
+        float x = fmaf(s[kb][r], cs, -msc);
+        if constexpr (ALIBI) x = fmaf(-bc, fabsf(dq - alibi_off(kb, r)), x);
+        return x;
+      };
+      float lsum = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        u32x4 u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kb = ks >> 1, r0 = 8 * (ks & 1) + 2 * i;
+          const f32x2 e = {fast_exp2(arg(kb, r0)), fast_exp2(arg(kb, r0 + 1))};
+          const bf16x2 h = __builtin_convertvector(e, bf16x2);
+          u[i] = __builtin_bit_cast(uint32_t, h);
+          // The dot operand is the converted pair itself: bit-casting it back out of u[i]
+          // makes this compiler feed the same register to every dot instruction.
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(h, ones2, lsum, false);
+        }
+        pp[ks] = as_bf16x8(u);
+      }
+      return lsum;
+    };
+
+    // The exponent offset m_run is the row max of the first tile in which the row sees a
+    // key, and stays fixed while every weight of a tile is at most 2^32 (checked through the
+    // tile's weight sum, which bounds each weight). A tile that breaks this (scores grown
+    // past the offset) is redone with the offset raised to its row max, after rescaling what
+    // was accumulated. Every term of a row always shares one offset, so the normalised
+    // result is that of the exact max.
+    auto tile = [&](int t, int u) {
+      f32x16 s[NKB];
+      qk(s, kslot(u));
+      issue(u + kAhead);
       prep(s, t);
-      const float m_new = fmaxf(m_run, row_max(s, t));
-      const float alpha = m_new == m_run ? 1.f : fast_exp2((m_run - m_new) * c);
-      l_run *= alpha;
+      if constexpr (WINDOW) {
+        if (wave_any(m_run == -INFINITY)) {  // rows that have not seen a key yet
+          const float mx = row_max(s, t);
+          if (m_run == -INFINITY) m_run = mx;  // stays -inf while all the row's keys are masked
+        }
+      } else if (t == 0) {
+        m_run = row_max(s, t);  // key 0 is visible to every row, so this is finite
+      }
+      bf16x8 pp[NKS];
+      float lsum = weights(s, pp, t);
+      if (wave_any(!(lsum <= kSumCap))) {
+        // Recompute the scores from the K tile (still in LDS) rather than keeping them live
+        // through the common path: the empty asm keeps the compiler from reusing them.
+        asm volatile("" ::: "memory");
+        qk(s, kslot(u));
+        prep(s, t);
+        const float m_new = fmaxf(m_run, row_max(s, t));
+        const float alpha = m_new == m_run ? 1.f : fast_exp2((m_run - m_new) * c);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        m_run = m_new;
+        lsum = weights(s, pp, t);
+      }
+      l_run += lsum;
+      pv(pp, vslot(u));
+    };
+
+    for (int t = t_first; t < ntiles; ++t, ++u) {
+      if (t >= wave_t0 && t < wave_nt)
+        tile(t, u);
+      else
+        issue(u + kAhead);
+      wait_vm<kJ * kAhead - kJ>();  // this wave's copies of position u + 1 have landed
+      block_barrier();              // ... and every wave's; slot u may be overwritten next
+    }
+
+    // Epilogue: O = O^T / l, rounded to bf16; LSE = m*|scale| + ln l.
+    const float l_tot = pair_sum(l_run);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (row_ok) {
+      uint16_t* orow = static_cast<uint16_t*>(p.o) + (((size_t)b * S + qi) * Hq + hq) * D;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      m_run = m_new;
-      lsum = weights(s, pp, t);
+        for (int j = 0; j < 4; ++j) {
+          const int d0 = db * 32 + 8 * j + 4 * hh;
+          u32x2 w;
+          w[0] = pack_bf16x2(oacc[db][4 * j + 0] * inv, oacc[db][4 * j + 1] * inv);
+          w[1] = pack_bf16x2(oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv);
+          *reinterpret_cast<u32x2*>(orow + d0) = w;
+        }
+      if (p.lse && hh == 0)
+        p.lse[((size_t)b * Hq + hq) * S + qi] =
+            l_tot > 0.f ? m_run * p.scale_abs + logf(l_tot) : -INFINITY;
     }
-    l_run += lsum;
-    pv(pp, vslot(t));
-  };
+  }
+  wait_vm<0>();  // drain the copies issued past the last tile
+}
 
-  // ---- pipeline: the DMA of tile t+3 is issued before tile t is computed; after tile t
-  // each wave waits for its own copies of tile t+1 and the barrier publishes everyone's.
-  const bool any_tile = t_first < ntiles;
-  if (any_tile) {
-#pragma unroll
-    for (int t = 0; t < kAhead; ++t) issue_tile(t_first + t);
-    wait_vm<kJ * (kAhead - 1)>();  // the first tile has landed
-  }
-  block_barrier();
-  for (int t = t_first; t < ntiles; ++t) {
-    issue_tile(t + kAhead);  // past the end: empty resource, zeros land in a free slot
-    if (t >= wave_t0 && t < wave_nt) tile(t);
-    wait_vm<kJ * kAhead - kJ>();  // this wave's copies of tile t+1 have landed
-    block_barrier();              // ... and every wave's; slot t may be overwritten next
-  }
-  if (any_tile) wait_vm<0>();  // drain the copies issued for tiles past the end
+// Dynamic LDS of the kernel: the K/V ring, then the length-order tables.
+template <int D>
+constexpr size_t prefill_lds_bytes() {
+  return PfLayout<D>::LDS_BYTES + 2 * kPrefillLptMaxB * sizeof(int);
+}
 
-  // Epilogue: O = O^T / l, rounded to bf16; LSE = m*|scale| + ln l.
-  const float l_tot = pair_sum(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (row_ok) {
-    uint16_t* orow = static_cast<uint16_t*>(p.o) + (((size_t)b * S + qi) * Hq + hq) * D;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d0 = db * 32 + 8 * j + 4 * hh;
-        u32x2 w;
-        w[0] = pack_bf16x2(oacc[db][4 * j + 0] * inv, oacc[db][4 * j + 1] * inv);
-        w[1] = pack_bf16x2(oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + d0) = w;
-      }
-    if (p.lse && hh == 0)
-      p.lse[((size_t)b * Hq + hq) * S + qi] =
-          l_tot > 0.f ? m_run * p.scale_abs + logf(l_tot) : -INFINITY;
-  }
+// Workgroups of one kernel that a CU holds at once (at least 1).
+template <typename K>
+int resident_per_cu(K kern, int threads, size_t lds) {
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+    return 1;
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, threads, lds) != hipSuccess) return 1;
+  return nb > 0 ? nb : 1;
 }
 
 template <int D, bool CAUSAL, bool WINDOW, bool ALIBI>
 hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
-  const size_t lds = PfLayout<D>::LDS_BYTES;
+  const size_t lds = prefill_lds_bytes<D>();
   auto kern = prefill_bf16_kernel<D, CAUSAL, WINDOW, ALIBI>;
+  static const int per_cu = resident_per_cu(kern, PfShape<D>::THREADS, lds);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(8 * p.per_xcd), dim3(PfShape<D>::THREADS), lds, stream, p);
+  int dev = 0, cus = 0;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+    return e;
+  // One resident workgroup per slot: P slots per XCD, each working through its share of
+  // the XCD's queue (no more slots than queue positions).
+  const int slots = PfShape<D>::PERSISTENT ? per_cu * (cus / 8 > 0 ? cus / 8 : 1) : p.per_xcd;
+  const int P = p.per_xcd < slots ? p.per_xcd : slots;
+  hipLaunchKernelGGL(kern, dim3(8 * (P > 0 ? P : 1)), dim3(PfShape<D>::THREADS), lds, stream, p);
   return hipGetLastError();
 }
 

@@ -84,6 +84,36 @@ def test_prefill_window_alibi(oracle_mod, dtype, d, window, alibi, causal):
         assert e <= TOL[dtype] and le <= LSE_TOL[dtype]
 
 
+NEG_CASES = [(dtype, d, w, a, c) for dtype in (torch.bfloat16, torch.float32)
+             for d in (32, 64, 128)
+             for (w, a, c) in ((0, False, False), (0, False, True), (40, True, True),
+                               (0, True, False))]
+
+
+@pytest.mark.parametrize("dtype,d,window,alibi,causal", NEG_CASES)
+def test_prefill_negative_scale(oracle_mod, dtype, d, window, alibi, causal):
+    """A negative softmax scale (the weights favour small dot products) with every option:
+    masked keys must still get weight 0 whatever the sign."""
+    B, S, Hq, Hkv = 2, 100, 4, 2
+    seed = 2600 + d + window + 7 * int(alibi) + int(causal)
+    _say(f"case prefill_ex negative scale {dtype} d={d} window={window} alibi={alibi} "
+         f"causal={causal}")
+    q, k, v = _rand((B, S, Hq, d), seed, dtype), _rand((B, S, Hkv, d), seed + 1, dtype), \
+        _rand((B, S, Hkv, d), seed + 2, dtype)
+    slopes = alibi_slopes(Hq) if alibi else None
+    scale = -0.7 / math.sqrt(d)
+    lens = [100, 37]
+    ld = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    o, lse = gqa.prefill(q.cuda(), k.cuda(), v.cuda(), causal=causal, softmax_scale=scale,
+                         seqlens=ld, window=window, alibi_slopes=slopes, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle_mod.prefill(q, k, v, scale=scale, causal=causal, seqlens=lens,
+                                window=window, alibi_slopes=slopes)
+    e, le = _errs(o, lse, ro, rl)
+    _say(f"  max_abs_err={e:.3e} lse_err={le:.3e}")
+    assert e <= TOL[dtype] and le <= LSE_TOL[dtype]
+
+
 def test_prefill_window_full_size_sampled(oracle_mod):
     """Causal Llama-shaped prefill (B=4, S=4096, 32/8 heads, d=128) with a 1000-key window and
     ALiBi, in the launch configuration the benchmark uses; 300 sampled rows."""
