@@ -131,6 +131,7 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
   constexpr int ROWS = Shp::ROWS;
   constexpr int PF_BN = Lay::BN;
   constexpr int NKB = Lay::NKB, NKS = Lay::NKS;
+  constexpr bool kBatchReads = D == 128;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
   // LDS: K slots 0..RING-1, then V slots 0..RING-1 (byte offsets).
@@ -387,32 +388,63 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) oacc[i] = zero16();
 
-    auto qk = [&](f32x16 (&s)[NKB], int slot_off) {
+    // S^T = K Q^T. For d = 128 all K fragments of the tile are read from LDS first and the
+    // products then run back to back (measured faster); for d <= 64 each read feeds its
+    // product directly, which keeps the register budget of four waves per SIMD.
+    auto qk = [&](f32x16 (&sc)[NKB], int slot_off) {
+      auto kfrag = [&](int ks, int kb) {
+        return *reinterpret_cast<const u32x4*>(smem + slot_off + kb * 32 * Lay::ROWB + k_lane +
+                                               16 * ((2 * ks) ^ k_swz));
+      };
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) s[kb] = zero16();
+      for (int kb = 0; kb < NKB; ++kb) sc[kb] = zero16();
+      if constexpr (kBatchReads) {
+        u32x4 kf[D / 16][NKB];
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
+        for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(smem + slot_off + kb * 32 * Lay::ROWB +
-                                                          k_lane + 16 * ((2 * ks) ^ k_swz));
-          s[kb] = mfma_bf16_32x32x16(as_bf16x8(a), qf[ks], s[kb]);
-        }
+          for (int kb = 0; kb < NKB; ++kb) kf[ks][kb] = kfrag(ks, kb);
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+            sc[kb] = mfma_bf16_32x32x16(as_bf16x8(kf[ks][kb]), qf[ks], sc[kb]);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+            sc[kb] = mfma_bf16_32x32x16(as_bf16x8(kfrag(ks, kb)), qf[ks], sc[kb]);
       }
     };
+    // O^T += V^T P^T, 16 keys per MFMA; B slot i <-> key 16ks + 8(i/4) + 4hh + (i%4). The
+    // V^T fragments come from transposing reads (batched first for d = 128, as for K).
     auto pv = [&](const bf16x8 (&pp)[NKS], int slot_off) {
+      auto vfrag = [&](int ks, int db) {
+        const int off = slot_off + ks * 16 * Lay::ROWB + v_lane + 16 * ((4 * db + tr_q) ^ v_swz);
+        const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(smem + off));
+        const s16x4 hi4 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(smem + off + 8 * Lay::ROWB));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo4), h2 = __builtin_bit_cast(u32x2, hi4);
+        return u32x4{l2[0], l2[1], h2[0], h2[1]};
+      };
+      if constexpr (kBatchReads) {
+        u32x4 vf[NKS][D / 32];
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
+        for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const int off = slot_off + ks * 16 * Lay::ROWB + v_lane + 16 * ((4 * db + tr_q) ^ v_swz);
-          const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(smem + off));
-          const s16x4 hi4 =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(smem + off + 8 * Lay::ROWB));
-          const u32x2 l2 = __builtin_bit_cast(u32x2, lo4), h2 = __builtin_bit_cast(u32x2, hi4);
-          const u32x4 a = {l2[0], l2[1], h2[0], h2[1]};
-          oacc[db] = mfma_bf16_32x32x16(as_bf16x8(a), pp[ks], oacc[db]);
-        }
+          for (int db = 0; db < D / 32; ++db) vf[ks][db] = vfrag(ks, db);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+            oacc[db] = mfma_bf16_32x32x16(as_bf16x8(vf[ks][db]), pp[ks], oacc[db]);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+            oacc[db] = mfma_bf16_32x32x16(as_bf16x8(vfrag(ks, db)), pp[ks], oacc[db]);
       }
     };
 
@@ -422,32 +454,31 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
     float m_run = WINDOW ? -INFINITY : 0.f, l_run = 0.f;
     // ALiBi: the score gets -slope_h * |i - j|, i.e. -beta * |i - j| in the units of the
     // raw dot product that c = |scale| * log2(e) scales into exp2 units.
-    float beta = 0.f;
-    if constexpr (ALIBI) beta = p.alibi[hq] * kLog2e / c;
+    const float beta = ALIBI ? p.alibi[hq] * kLog2e / c : 0.f;
 
-    // Key j = t0 + 32kb + 8(r/4) + 4hh + (r%4) is kept iff lo <= j < lim: the signs of
-    // j - lim and j - lo select between the score and -inf bit patterns (no compare masks
-    // in SGPRs).
-    auto mask = [&](f32x16 (&s)[NKB], int t0) {
+    // Key j = t0 + 32kb + 8(i/4) + 4hh + (i%4) is kept iff lo <= j < lim: the signs of
+    // j - lim and j - lo select between the score and the masked bit pattern (no compare
+    // masks in SGPRs).
+    auto mask = [&](f32x16 (&sc)[NKB], int t0) {
       const int base = t0 + 4 * hh - lim;
       const int base_lo = t0 + 4 * hh - lo;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int jj = 32 * kb + 8 * (r >> 2) + (r & 3);
+        for (int i = 0; i < 16; ++i) {
+          const int jj = 32 * kb + 8 * (i >> 2) + (i & 3);
           uint32_t keep = (uint32_t)((base + jj) >> 31);
           if constexpr (WINDOW) keep &= ~(uint32_t)((base_lo + jj) >> 31);
-          s[kb][r] = __uint_as_float((__float_as_uint(s[kb][r]) & keep) | (masked_bits & ~keep));
+          sc[kb][i] = __uint_as_float((__float_as_uint(sc[kb][i]) & keep) | (masked_bits & ~keep));
         }
     };
     // Mask tile t's scores if any key of the wave's rows is masked in it.
-    auto prep = [&](f32x16 (&s)[NKB], int t) {
+    auto prep = [&](f32x16 (&sc)[NKB], int t) {
       const int t0 = t * PF_BN;
-      if (t0 + PF_BN > wave_mask_from || (WINDOW && t0 < wave_lo_hi)) mask(s, t0);
+      if (t0 + PF_BN > wave_mask_from || (WINDOW && t0 < wave_lo_hi)) mask(sc, t0);
     };
-    // ALiBi distance |i - j| of this lane's score (kb, r) in tile t: key j = t0 + 32kb +
-    // 8(r/4) + 4hh + (r%4), so i - j = dq(t) - (32kb + 8(r/4) + r%4).
+    // ALiBi distance |i - j| of this lane's score (kb, i) in tile t: key j = t0 + 32kb +
+    // 8(i/4) + 4hh + (i%4), so i - j = dq(t) - (32kb + 8(i/4) + i%4).
     // (The empty asm hides where dq came from, so the compiler recomputes the distances in
     // each use instead of keeping 32 of them live between the row max and the weights.)
     auto alibi_dq = [&](int t) {
@@ -455,49 +486,49 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
       asm volatile("" : "+v"(dq));
       return dq;
     };
-    auto alibi_off = [](int kb, int r) { return (float)(32 * kb + 8 * (r >> 2) + (r & 3)); };
+    auto alibi_off = [](int kb, int i) { return (float)(32 * kb + 8 * (i >> 2) + (i & 3)); };
     // Row max of the (signed, biased) scores over the tile (the row's other keys sit in lane
     // l ^ 32).
-    auto row_max = [&](const f32x16 (&s)[NKB], int t) {
+    auto row_max = [&](const f32x16 (&sc)[NKB], int t) {
       float mx = -INFINITY;
       const float dq = ALIBI ? alibi_dq(t) : 0.f;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = s[kb][r] * sgn;
-          if constexpr (ALIBI) x = fmaf(-beta, fabsf(dq - alibi_off(kb, r)), x);
+        for (int i = 0; i < 16; ++i) {
+          float x = sc[kb][i] * sgn;
+          if constexpr (ALIBI) x = fmaf(-beta, fabsf(dq - alibi_off(kb, i)), x);
           mx = fmaxf(mx, x);
         }
       return pair_max(mx);
     };
     // Weights exp2(c sgn s - c m) rounded to bf16 as the PV operand; returns this lane's sum
     // of the rounded weights (the same values the PV product uses). exp2(-inf) = 0.
-    auto weights = [&](const f32x16 (&s)[NKB], bf16x8 (&pp)[NKS], int t) {
+    auto weights = [&](const f32x16 (&sc)[NKB], bf16x8 (&pp)[NKS], int t) {
       const float msc = ((WINDOW && m_run == -INFINITY) ? 0.f : m_run) * c;  // no key yet
       const float dq = ALIBI ? alibi_dq(t) : 0.f;
       const float bc = beta * c;  // the bias slope in exp2 units
-      // exp2 argument of score (kb, r): c * (sgn s - beta |i - j|) - c * m
-      auto arg = [&](int kb, int r) {
-        float x = fmaf(s[kb][r], cs, -msc);
-        if constexpr (ALIBI) x = fmaf(-bc, fabsf(dq - alibi_off(kb, r)), x);
+      // exp2 argument of score (kb, i): c * (sgn s - beta |i - j|) - c * m
+      auto arg = [&](int kb, int i) {
+        float x = fmaf(sc[kb][i], cs, -msc);
+        if constexpr (ALIBI) x = fmaf(-bc, fabsf(dq - alibi_off(kb, i)), x);
         return x;
       };
       float lsum = 0.f;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        u32x4 u;
+        u32x4 w;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int kb = ks >> 1, r0 = 8 * (ks & 1) + 2 * i;
-          const f32x2 e = {fast_exp2(arg(kb, r0)), fast_exp2(arg(kb, r0 + 1))};
+          const int kb = ks >> 1, i0 = 8 * (ks & 1) + 2 * i;
+          const f32x2 e = {fast_exp2(arg(kb, i0)), fast_exp2(arg(kb, i0 + 1))};
           const bf16x2 h = __builtin_convertvector(e, bf16x2);
-          u[i] = __builtin_bit_cast(uint32_t, h);
-          // The dot operand is the converted pair itself: bit-casting it back out of u[i]
+          w[i] = __builtin_bit_cast(uint32_t, h);
+          // The dot operand is the converted pair itself: bit-casting it back out of w[i]
           // makes this compiler feed the same register to every dot instruction.
           lsum = __builtin_amdgcn_fdot2_f32_bf16(h, ones2, lsum, false);
         }
-        pp[ks] = as_bf16x8(u);
+        pp[ks] = as_bf16x8(w);
       }
       return lsum;
     };
@@ -509,35 +540,35 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
     // was accumulated. Every term of a row always shares one offset, so the normalised
     // result is that of the exact max.
     auto tile = [&](int t, int u) {
-      f32x16 s[NKB];
-      qk(s, kslot(u));
+      f32x16 sc[NKB];
+      qk(sc, kslot(u));
       issue(u + kAhead);
-      prep(s, t);
+      prep(sc, t);
       if constexpr (WINDOW) {
         if (wave_any(m_run == -INFINITY)) {  // rows that have not seen a key yet
-          const float mx = row_max(s, t);
+          const float mx = row_max(sc, t);
           if (m_run == -INFINITY) m_run = mx;  // stays -inf while all the row's keys are masked
         }
       } else if (t == 0) {
-        m_run = row_max(s, t);  // key 0 is visible to every row, so this is finite
+        m_run = row_max(sc, t);  // key 0 is visible to every row, so this is finite
       }
       bf16x8 pp[NKS];
-      float lsum = weights(s, pp, t);
+      float lsum = weights(sc, pp, t);
       if (wave_any(!(lsum <= kSumCap))) {
         // Recompute the scores from the K tile (still in LDS) rather than keeping them live
         // through the common path: the empty asm keeps the compiler from reusing them.
         asm volatile("" ::: "memory");
-        qk(s, kslot(u));
-        prep(s, t);
-        const float m_new = fmaxf(m_run, row_max(s, t));
+        qk(sc, kslot(u));
+        prep(sc, t);
+        const float m_new = fmaxf(m_run, row_max(sc, t));
         const float alpha = m_new == m_run ? 1.f : fast_exp2((m_run - m_new) * c);
         l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
         m_run = m_new;
-        lsum = weights(s, pp, t);
+        lsum = weights(sc, pp, t);
       }
       l_run += lsum;
       pv(pp, vslot(u));
