@@ -553,7 +553,12 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
         m_run = row_max(sc, t);  // key 0 is visible to every row, so this is finite
       }
       bf16x8 pp[NKS];
+      // The softmax runs at raised wave priority, so a SIMD prefers this wave's vector work
+      // while other waves' matrix products are in flight (measured ~2% faster for d = 128,
+      // neutral for d = 64).
+      __builtin_amdgcn_s_setprio(1);
       float lsum = weights(sc, pp, t);
+      __builtin_amdgcn_s_setprio(0);
       if (wave_any(!(lsum <= kSumCap))) {
         // Recompute the scores from the K tile (still in LDS) rather than keeping them live
         // through the common path: the empty asm keeps the compiler from reusing them.
