@@ -16,7 +16,7 @@
 //     a normalised fp32 partial and its LSE to slot (w + u) (w and u never both
 //     decrease along the tile order, so w + u is unique), and the combine kernel
 //     merges a unit's partials in workgroup order with weights exp(lse_s - max).
-// Inside a workgroup the 4 waves take the segment's tiles round-robin and merge
+// Inside a workgroup the 8 waves take the segment's tiles round-robin and merge
 // their running (max, sum, O) through LDS.
 //
 // Per 32-key tile, per wave (lane l: query l % 32 of the block, key half l / 32):
@@ -33,7 +33,7 @@
 namespace gqa {
 namespace {
 
-constexpr int DC_WAVES = 4;
+constexpr int DC_WAVES = 8;  // one workgroup fills a CU (2 waves per SIMD)
 constexpr int DC_THREADS = 64 * DC_WAVES;
 constexpr int DC_TILE = 32;
 
@@ -365,17 +365,25 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_split_kernel(DecodeParam
       s_m[wave * 32 + l32] = m_run;
       s_l[wave * 32 + l32] = l_tot;
     }
+    // Accumulator slot r of the DPL column blocks holds columns DPL * (8(r/4) + 4hh + r%4)
+    // + 0 .. DPL-1: one vector store each.
 #pragma unroll
-    for (int cc = 0; cc < DPL; ++cc)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int d = DPL * (8 * (r >> 2) + 4 * hh + (r & 3)) + cc;
-        s_o[(wave * 32 + l32) * Lay::OSTR + d] = oacc[cc][r];
+    for (int r = 0; r < 16; ++r) {
+      float* dst = s_o + (wave * 32 + l32) * Lay::OSTR + DPL * (8 * (r >> 2) + 4 * hh + (r & 3));
+      if constexpr (DPL == 4) {
+        *reinterpret_cast<u32x4*>(dst) =
+            u32x4{__float_as_uint(oacc[0][r]), __float_as_uint(oacc[1][r]),
+                  __float_as_uint(oacc[2][r]), __float_as_uint(oacc[3][r])};
+      } else {
+        *reinterpret_cast<u32x2*>(dst) = u32x2{__float_as_uint(oacc[0][r]), __float_as_uint(oacc[1][r])};
       }
+    }
     __syncthreads();
     {
-      const int n = tid >> 3;                 // query of the block
-      const int dseg = (tid & 7) * (D / 8);   // D/8 output columns per thread
+      constexpr int SEGS = DC_THREADS / 32;  // threads per query row
+      constexpr int CPT = D / SEGS;          // output columns per thread
+      const int n = tid / SEGS;              // query of the block
+      const int dseg = (tid % SEGS) * CPT;
       float M = -INFINITY;
 #pragma unroll
       for (int wv = 0; wv < DC_WAVES; ++wv) M = fmaxf(M, s_m[wv * 32 + n]);
@@ -390,36 +398,41 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_split_kernel(DecodeParam
       const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
       const float lse_v = lsum > 0.f ? M * p.scale_abs + logf(lsum) : -INFINITY;
       if (n < nh) {
-        float val[D / 8];
+        float val[CPT];
 #pragma unroll
-        for (int dd = 0; dd < D / 8; ++dd) {
-          float acc = 0.f;
+        for (int dd = 0; dd < CPT; ++dd) val[dd] = 0.f;
 #pragma unroll
-          for (int wv = 0; wv < DC_WAVES; ++wv)
-            acc += wgt[wv] * s_o[(wv * 32 + n) * Lay::OSTR + dseg + dd];
-          val[dd] = acc * inv;
-        }
+        for (int wv = 0; wv < DC_WAVES; ++wv)
+#pragma unroll
+          for (int q4 = 0; q4 < CPT / 4; ++q4) {
+            const u32x4 x =
+                *reinterpret_cast<const u32x4*>(s_o + (wv * 32 + n) * Lay::OSTR + dseg + 4 * q4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) val[4 * q4 + e] += wgt[wv] * __uint_as_float(x[e]);
+          }
+#pragma unroll
+        for (int dd = 0; dd < CPT; ++dd) val[dd] *= inv;
         if (ta == 0 && te == Tb) {
           uint16_t* orow = static_cast<uint16_t*>(p.o) + ((size_t)b * p.Hq + hbase + n) * D + dseg;
 #pragma unroll
-          for (int q4 = 0; q4 < D / 64; ++q4) {
-            u32x4 wv4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) wv4[e] = pack_bf16x2(val[8 * q4 + 2 * e], val[8 * q4 + 2 * e + 1]);
-            *reinterpret_cast<u32x4*>(orow + 8 * q4) = wv4;
+          for (int q4 = 0; q4 < CPT / 4; ++q4) {
+            u32x2 w2;
+            w2[0] = pack_bf16x2(val[4 * q4], val[4 * q4 + 1]);
+            w2[1] = pack_bf16x2(val[4 * q4 + 2], val[4 * q4 + 3]);
+            *reinterpret_cast<u32x2*>(orow + 4 * q4) = w2;
           }
-          if (p.lse && (tid & 7) == 0) p.lse[(size_t)b * p.Hq + hbase + n] = lse_v;
+          if (p.lse && (tid % SEGS) == 0) p.lse[(size_t)b * p.Hq + hbase + n] = lse_v;
         } else {
           const size_t slot = (size_t)w + u;
           float* dst = p.ws_o + (slot * 32 + n) * D + dseg;
 #pragma unroll
-          for (int q4 = 0; q4 < D / 32; ++q4) {
+          for (int q4 = 0; q4 < CPT / 4; ++q4) {
             u32x4 wv4;
 #pragma unroll
             for (int e = 0; e < 4; ++e) wv4[e] = __float_as_uint(val[4 * q4 + e]);
             *reinterpret_cast<u32x4*>(dst + 4 * q4) = wv4;
           }
-          if ((tid & 7) == 0) p.ws_lse[slot * 32 + n] = lse_v;
+          if ((tid % SEGS) == 0) p.ws_lse[slot * 32 + n] = lse_v;
         }
       }
     }

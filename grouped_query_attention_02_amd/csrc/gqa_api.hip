@@ -14,7 +14,7 @@ namespace {
 
 constexpr int kVersion = 10000;  // 1.0.0
 constexpr int kDecodeTile = 32;  // keys per decode tile
-constexpr int kDecodeAutoShares = 512;  // auto split: at least 2 workgroups per CU of a 256-CU GPU
+constexpr int kDecodeAutoShares = 256;  // auto split: one 8-wave workgroup per CU of a 256-CU GPU
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kMinScaleLog2 = 1e-30f;
 

@@ -93,11 +93,11 @@ def test_decode_rejects(lib, kw, code):
 
 
 def test_decode_plan_rule(lib):
-    """Auto rule: max(units, 512) shares, capped at one share per 32-key tile; n splits: n*units."""
+    """Auto rule: max(units, 256) shares, capped at one share per 32-key tile; n splits: n*units."""
     def units(B, Hq, Hkv):
         return B * Hkv * -(-(Hq // Hkv) // 32)
-    # 32 sequences x 1 K/V head, 32 heads: 32 units -> 512 shares
-    assert gqa.decode_num_workgroups(32, 32, 1, 32768, 0) == 512
+    # 32 sequences x 1 K/V head, 32 heads: 32 units -> 256 shares
+    assert gqa.decode_num_workgroups(32, 32, 1, 32768, 0) == 256
     # 64 x 8 units (uniform 8k caches): one share per unit
     assert gqa.decode_num_workgroups(64, 64, 8, 8192, 0) == 512
     # tiny caches cap the shares at the tile count
@@ -107,7 +107,7 @@ def test_decode_plan_rule(lib):
     assert units(3, 64, 1) == 6
     assert gqa.decode_num_workgroups(3, 64, 1, 64, 0) == 6 * 2
     # workspace = (shares + units) slots x 32 heads x (d + 1) floats
-    W, U = 512, 32
+    W, U = 256, 32
     assert gqa.decode_workspace_bytes(32, 32, 1, 128, 32768, 0) == (W + U) * 32 * 129 * 4
     assert gqa.decode_workspace_bytes(32, 32, 1, 128, 0, 0) == 0
     assert gqa.decode_workspace_bytes(32, 30, 4, 128, 100, 0) == 0
