@@ -319,6 +319,34 @@ def test_decode_deterministic():
         assert torch.equal(gqa.decode(q, kc, vc, lens), first)
 
 
+def test_decode_reused_garbage_workspace(oracle_mod):
+    """The workspace's contents on entry do not matter: one holding garbage, and one reused
+    across calls with other lengths and split counts, gives the same bits as a fresh one."""
+    B, Hq, Hkv, d, max_len = 7, 32, 1, 128, 3000
+    q = _rand((B, Hq, d), 95, torch.bfloat16).cuda()
+    kc = _rand((B, Hkv, max_len, d), 96, torch.bfloat16).cuda()
+    vc = _rand((B, Hkv, max_len, d), 97, torch.bfloat16).cuda()
+    need = max(gqa.decode_workspace_bytes(B, Hq, Hkv, d, max_len, s) for s in (0, 3, 9))
+    g = torch.Generator().manual_seed(98)
+    ws = torch.randint(0, 256, (need,), generator=g, dtype=torch.uint8).cuda()
+    cases = [([3000, 1, 0, 1700, 33, 2999, 64], 0), ([5, 3000, 2500, 0, 1, 32, 1000], 3),
+             ([3000, 1, 0, 1700, 33, 2999, 64], 9), ([100, 100, 100, 100, 100, 100, 100], 0)]
+    for rep in range(2):
+        for lens, splits in cases:
+            _say(f"case decode reused workspace rep={rep} lens={lens} splits={splits}")
+            ld = torch.tensor(lens, dtype=torch.int32).cuda()
+            o, lse = gqa.decode(q, kc, vc, ld, softmax_scale=0.09, num_splits=splits,
+                                return_lse=True, workspace=ws)
+            fo, flse = gqa.decode(q, kc, vc, ld, softmax_scale=0.09, num_splits=splits,
+                                  return_lse=True)
+            torch.cuda.synchronize()
+            assert torch.equal(o, fo) and torch.equal(lse, flse)
+            ref_o, ref_l = oracle_mod.decode(q.cpu(), kc.cpu(), vc.cpu(), scale=0.09, lens=lens)
+            assert _max_err(o, ref_o) <= 2e-2 and _lse_err(lse, ref_l) <= BF16_DECODE_LSE_TOL
+        if rep == 0:
+            ws.fill_(255)
+
+
 _DEC_CACHE = {}
 
 
