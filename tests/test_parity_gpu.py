@@ -120,6 +120,7 @@ def test_prefill_edge_lengths_and_scales(oracle_mod, dtype):
 
 
 @pytest.mark.parametrize("B,S,Hq,Hkv,d", [(40, 70, 4, 2, 64), (19, 130, 6, 3, 128),
+                                           (100, 40, 4, 2, 64), (90, 50, 8, 2, 128),
                                            (300, 20, 2, 1, 32)])
 def test_prefill_many_ragged_sequences(oracle_mod, B, S, Hq, Hkv, d):
     """Many sequences with repeated, zero and over-long lengths: the bf16 kernel orders its
