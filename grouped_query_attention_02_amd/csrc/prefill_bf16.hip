@@ -1,12 +1,13 @@
 // prefill_bf16.hip - bf16 grouped-query attention prefill on gfx950 matrix cores.
 //
-// Work split: one workgroup per (sequence b, K/V head kvh, block of flattened query
-// rows). A flattened row f = i * g + h_local stands for query position i of head
-// kvh * g + h_local, so every row of a block reads the same K/V head (kv_head = q_head /
-// g, blog.gitcode.com "3个GQA核心优化技巧", section "Flash-Attention的稀疏分组优化") and
-// each K/V tile is staged in LDS once and reused by all g heads of the group (same
-// section: K/V reuse in on-chip memory, access granularity raised from a head to a
-// block).
+// Work split: one work item per (sequence b, K/V head kvh, block of flattened query
+// rows), one workgroup per item (d <= 64) or a resident workgroup working through a
+// share of the items (d = 128). A flattened row f = i * g + h_local stands for query
+// position i of head kvh * g + h_local, so every row of a block reads the same K/V head
+// (kv_head = q_head / g, blog.gitcode.com "3个GQA核心优化技巧", section
+// "Flash-Attention的稀疏分组优化") and each K/V tile is staged in LDS once and reused by
+// all g heads of the group (same section: K/V reuse in on-chip memory, access
+// granularity raised from a head to a block).
 //
 // Per K/V tile (64 keys, 32 for d = 128), each wave (32 rows) computes
 //   S^T = K Q^T          (A = K rows from LDS, B = Q held in VGPRs)
@@ -18,7 +19,7 @@
 //                        accumulators)
 // on v_mfma_f32_32x32x16_bf16. The kernel is kept small (at most 128 VGPRs for d <= 64)
 // so that several waves share each SIMD and the hardware overlaps one wave's matrix
-// products with another wave's softmax. K/V tiles stream from HBM/L2 straight into an
+// products with another wave's softmax. K/V tiles stream from HBM/L2 straight into a
 // 4-slot LDS ring, three tiles ahead of their use. The exponent offset is a row
 // max that is raised only when a tile's weights would exceed 2^32, so the O rescale is
 // rare; every term of a row always shares one offset, so the normalised result is
