@@ -300,6 +300,64 @@ def _recorded_traffic(summary_name, source_name):
         return None
 
 
+def _achievable(dev) -> dict:
+    """Achievable peaks on this GPU from libgqa_probes.so: back-to-back bf16 32x32x16 MFMAs
+    (four independent chains per wave, four waves per SIMD) and a read of a 4 GiB buffer
+    (16 x the last-level cache), each the best of several timed launches."""
+    import ctypes
+    import torch
+    from grouped_query_attention_02_amd import build as gbuild
+    if not os.path.exists(gbuild.PROBES_LIB):
+        raise RuntimeError(f"{gbuild.PROBES_LIB} is missing: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(gbuild.PROBES_LIB, mode=ctypes.RTLD_LOCAL)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int
+    lib.gqa_probe_mfma_flops.argtypes = [i32, i32]
+    lib.gqa_probe_mfma_flops.restype = ctypes.c_double
+    lib.gqa_probe_mfma_bf16.argtypes = [i32, i32, vp, vp]
+    lib.gqa_probe_read.argtypes = [vp, ctypes.c_size_t, vp, i32, vp]
+    stream = torch.cuda.current_stream().cuda_stream
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    blocks, iters = 4 * cus, 400
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+
+    def best(fn, reps):
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            if fn() != 0:
+                raise RuntimeError("probe launch failed")
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return min(ts)
+
+    def mfma():
+        return lib.gqa_probe_mfma_bf16(blocks, iters, out.data_ptr(), stream)
+
+    best(mfma, 3)
+    ms = best(mfma, 5)
+    tflops = lib.gqa_probe_mfma_flops(blocks, iters) / (ms * 1e-3) / 1e12
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.zero_()
+    rblocks = 16 * cus
+    rout = torch.empty(rblocks * 256, dtype=torch.int32, device=dev)
+
+    def rd():
+        return lib.gqa_probe_read(buf.data_ptr(), nbytes // 16, rout.data_ptr(), rblocks, stream)
+
+    gbps = 0.0
+    for per_cu in (4, 8, 16):  # the best of a few grid sizes
+        rblocks = per_cu * cus
+        best(rd, 2)
+        gbps = max(gbps, nbytes / (best(rd, 5) * 1e-3) / 1e9)
+    del buf, rout, out
+    torch.cuda.empty_cache()
+    return {"mfma_bf16_tflops": round(tflops, 1), "hbm_read_gbps": round(gbps, 1),
+            "source": "probes/probes.hip: back-to-back bf16 MFMA; 4 GiB streaming read"}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -401,6 +459,10 @@ def main(argv=None):
                                     "tflops": tc["flops"] / (statistics.mean(ms) * 1e-3) / 1e12}
         also.update(_extended_rows(args.steps, dev))
 
+    ach = _achievable(dev)
+    print(f"[bench] achievable: {ach['mfma_bf16_tflops']} TFLOP/s bf16 MFMA, "
+          f"{ach['hbm_read_gbps']} GB/s HBM read", file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
@@ -439,14 +501,17 @@ def main(argv=None):
             "traffic": _recorded_traffic("prefill_bert_base_traffic.md", "prefill_bf16.hip"),
             "kernel": "prefill_bf16_kernel<64, false, false, false>",
             "launch_us_mean": round(p_avg * 1e3, 2), "flops_per_launch": pc["flops"],
+            "frac_of_achievable": round(p_tflops / ach["mfma_bf16_tflops"], 4),
         },
         "decode": {
             "gbps": round(d_gbps, 2), "frac_hbm_peak": round(d_gbps / perfmodel.PEAK_HBM_GBPS, 4),
             "peak_gbps": perfmodel.PEAK_HBM_GBPS, "call_us_mean": round(d_avg * 1e3, 2),
             "call_us_min": round(min(d_ms) * 1e3, 2), "bytes_per_call": dc["bytes"],
+            "frac_of_achievable_read": round(d_gbps / ach["hbm_read_gbps"], 4),
             "kernels": "decode_split_kernel<128, false, false> + decode_combine_kernel<128>",
         },
         "cpu_baseline": cpu,
+        "achievable": ach,
         "also": also,
         "context": "pages: ~980 tokens/s for a whole BERT-base model on A100 at seq 1024, "
                    "batch 32, precision unstated; not comparable to an attention-kernel rate",

@@ -3,8 +3,9 @@
     python -m grouped_query_attention_02_amd.build
 
 Every HIP source under csrc/ is compiled to an object in _build/ (in parallel)
-and linked into grouped_query_attention_02_amd/libgqa.so. The packed-fp32
-target feature is switched off for all device code.
+and linked into grouped_query_attention_02_amd/libgqa.so; probes/probes.hip (the
+microbenchmarks bench.py compares against) becomes libgqa_probes.so. The
+packed-fp32 target feature is switched off for all device code.
 """
 from __future__ import annotations
 
@@ -20,6 +21,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgqa.so")
+PROBES_SRC = os.path.join(PKG, "probes", "probes.hip")
+PROBES_LIB = os.path.join(PKG, "libgqa_probes.so")
 ARCH = os.environ.get("GQA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -56,8 +59,14 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    ptmp = PROBES_LIB + f".tmp{os.getpid()}"
+    cmd = [HIPCC, *CFLAGS, "-shared", PROBES_SRC, "-o", ptmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"probe build failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(ptmp, PROBES_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBES_LIB}")
     return LIB
 
 
