@@ -9,9 +9,10 @@ One step = one pass of the whole hot path on resident, seeded synthetic inputs:
 the line's `decode` object carries the decode KV-cache GB/s; both are timed with HIP
 events on the stream the kernels run on, inside the K timed steps. After the timed
 steps, the causal Llama-style prefill and the uniform 8k decode are timed the same way
-and reported under `also` (not part of `value`).
+and reported under `also` (not part of `value`), and two microbenchmarks give the rates
+this GPU reaches (`achievable`: bf16 MFMA loop, streaming HBM read).
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra] [--no-probes]
     python bench.py --only prefill|decode|copy --steps K     (work for rocprofv3 runs)
     python bench.py --summarize-kernels DIR | --summarize-pmc DIR
 """
@@ -317,7 +318,7 @@ def _achievable(dev) -> dict:
     lib.gqa_probe_read.argtypes = [vp, ctypes.c_size_t, vp, i32, vp]
     stream = torch.cuda.current_stream().cuda_stream
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    blocks, iters = 4 * cus, 400
+    blocks, iters = 4 * cus, 1000
     out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
 
     def best(fn, reps):
@@ -336,7 +337,7 @@ def _achievable(dev) -> dict:
         return lib.gqa_probe_mfma_bf16(blocks, iters, out.data_ptr(), stream)
 
     best(mfma, 3)
-    ms = best(mfma, 5)
+    ms = best(mfma, 8)
     tflops = lib.gqa_probe_mfma_flops(blocks, iters) / (ms * 1e-3) / 1e12
     nbytes = 4 << 30
     buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -367,6 +368,8 @@ def main(argv=None):
                          "GPU clocks settle at their sustained level")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the extra workloads")
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the achievable-peak microbenchmarks (achievable = null)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--only", choices=["prefill", "decode", "copy"],
                     help="profiling run: execute just this work --steps times and exit")
@@ -459,9 +462,11 @@ def main(argv=None):
                                     "tflops": tc["flops"] / (statistics.mean(ms) * 1e-3) / 1e12}
         also.update(_extended_rows(args.steps, dev))
 
-    ach = _achievable(dev)
-    print(f"[bench] achievable: {ach['mfma_bf16_tflops']} TFLOP/s bf16 MFMA, "
-          f"{ach['hbm_read_gbps']} GB/s HBM read", file=sys.stderr, flush=True)
+    ach = None
+    if not args.no_probes:
+        ach = _achievable(dev)
+        print(f"[bench] achievable: {ach['mfma_bf16_tflops']} TFLOP/s bf16 MFMA, "
+              f"{ach['hbm_read_gbps']} GB/s HBM read", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -501,13 +506,13 @@ def main(argv=None):
             "traffic": _recorded_traffic("prefill_bert_base_traffic.md", "prefill_bf16.hip"),
             "kernel": "prefill_bf16_kernel<64, false, false, false>",
             "launch_us_mean": round(p_avg * 1e3, 2), "flops_per_launch": pc["flops"],
-            "frac_of_achievable": round(p_tflops / ach["mfma_bf16_tflops"], 4),
+            "frac_of_achievable": round(p_tflops / ach["mfma_bf16_tflops"], 4) if ach else None,
         },
         "decode": {
             "gbps": round(d_gbps, 2), "frac_hbm_peak": round(d_gbps / perfmodel.PEAK_HBM_GBPS, 4),
             "peak_gbps": perfmodel.PEAK_HBM_GBPS, "call_us_mean": round(d_avg * 1e3, 2),
             "call_us_min": round(min(d_ms) * 1e3, 2), "bytes_per_call": dc["bytes"],
-            "frac_of_achievable_read": round(d_gbps / ach["hbm_read_gbps"], 4),
+            "frac_of_achievable_read": round(d_gbps / ach["hbm_read_gbps"], 4) if ach else None,
             "kernels": "decode_split_kernel<128, false, false> + decode_combine_kernel<128>",
         },
         "cpu_baseline": cpu,
