@@ -41,7 +41,7 @@ extern "C" {
 typedef enum {
     GQA_OK = 0,
     GQA_ERR_INVALID_ARG = 1, /* bad shape, NULL required pointer, misalignment, H_q % H_kv != 0 */
-    GQA_ERR_UNSUPPORTED = 2, /* head size or dtype this build does not provide             */
+    GQA_ERR_UNSUPPORTED = 2, /* head size or dtype the library does not provide            */
     GQA_ERR_WORKSPACE = 3,   /* decode workspace missing or smaller than required           */
     GQA_ERR_HIP = 4          /* the HIP runtime reported an error at launch                 */
 } gqa_status_t;
