@@ -253,9 +253,16 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
     const int q = pos ^ (is_k ? Lay::fk(row) : Lay::fv(row));
     voff[j] = (uint32_t)row * row_bytes + 16u * q;
   }
-  // Issue cursor: the next tile to copy is tile it_t of item it_k (tiles up to it_end);
-  // it_kp / it_vp point at the item's K and V rows, it_L is its length.
-  int it_k = -1, it_t = 0, it_end = 0, it_L = 0;
+  // Causal ALiBi visits an item's key tiles nearest-first (from the diagonal down to key
+  // 0): the bias then only falls from one tile to the next, so the exponent offset taken
+  // from the first tile a row sees keys in stays above the later tiles' scores as it does
+  // without a bias. (In key order each tile nearer the diagonal would raise the scores by
+  // up to slope * tile width and could force the redo below on many tiles.)
+  constexpr bool kNearFirst = CAUSAL && ALIBI;
+  // Issue cursor: the next tile to copy is position it_t of item it_k's tiles [it_first,
+  // it_end) (key tile it_t, or it_first + it_end - 1 - it_t when nearest-first); it_kp /
+  // it_vp point at the item's K and V rows, it_L is its length.
+  int it_k = -1, it_t = 0, it_first = 0, it_end = 0, it_L = 0;
   bool live = true;
   const uint16_t* it_kp = k_all;
   const uint16_t* it_vp = v_all;
@@ -272,6 +279,7 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
       item_tiles(n, t0, nt);
       if (t0 < nt) {
         it_t = t0;
+        it_first = t0;
         it_end = nt;
         it_L = n.Lb;
         it_kp = k_all + ((size_t)n.b * S * Hkv + n.kvh) * D;
@@ -284,7 +292,8 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
   // has an empty resource and zeros land in the (free) slot: every wave issues the same
   // number of copies per ring position, which keeps the waits below exact.
   auto issue = [&](int u) {
-    const int t0 = it_t * PF_BN;
+    // (past the last tile it_L is 0, so the copy is empty whatever tile it names)
+    const int t0 = (kNearFirst && live ? it_first + it_end - 1 - it_t : it_t) * PF_BN;
     const uint32_t valid = (uint32_t)max(it_L - t0, 0) * row_bytes;
     const i32x4 rk = make_rsrc(it_kp + (size_t)t0 * rstride, valid);
     const i32x4 rv = make_rsrc(it_vp + (size_t)t0 * rstride, valid);
@@ -389,6 +398,25 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) oacc[i] = zero16();
 
+    // ALiBi: the score gets -slope_h * |i - j|, i.e. -beta * |i - j| in the units of the
+    // raw dot product that c = |scale| * log2(e) scales into exp2 units.
+    const float slope = ALIBI ? p.alibi[hq] : 0.f;
+    const float beta = slope * kLog2e / c;
+    // The bias is measured from key qa = min(i, L_b - 1), the visible key nearest to the
+    // query: when i >= L_b every key lies below qa, so |i - j| = |qa - j| + (i - qa). The
+    // constant slope * (i - qa) drops out of the softmax and is added back to the LSE; it
+    // keeps the offsets of rows far past a short key range near the size of their scores.
+    const int qa = ALIBI ? min(qi, Lb - 1) : qi;
+    // Causal ALiBi is linear in the key: every visible key has j <= qa, so the bias is
+    // beta * (j - qa) = beta * (t0 + 4hh - qa) + beta * jj(kb, r), a per-tile term plus a
+    // per-slot term that does not change between tiles. The per-slot term starts the score
+    // accumulators (the products add onto it: sgn * jj * beta, so that sgn * s comes out
+    // biased), and the per-tile term joins the exponent offset, so the bias costs no
+    // instruction per score. Masked keys are overwritten by the mask.
+    constexpr bool kLinBias = CAUSAL && ALIBI;
+    const float sbeta = sgn * beta;
+    auto alibi_off = [](int kb, int i) { return (float)(32 * kb + 8 * (i >> 2) + (i & 3)); };
+
     // S^T = K Q^T. For d = 128 all K fragments of the tile are read from LDS first and the
     // products then run back to back (measured faster); for d <= 64 each read feeds its
     // product directly, which keeps the register budget of four waves per SIMD.
@@ -397,8 +425,18 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
         return *reinterpret_cast<const u32x4*>(smem + slot_off + kb * 32 * Lay::ROWB + k_lane +
                                                16 * ((2 * ks) ^ k_swz));
       };
+      if constexpr (kLinBias) {
+        float sb = sbeta;
+        // (d <= 64: recomputed per tile rather than kept live across the loop)
+        if constexpr (D <= 64) asm volatile("" : "+v"(sb));
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) sc[kb] = zero16();
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sc[kb][i] = sb * alibi_off(kb, i);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) sc[kb] = zero16();
+      }
       if constexpr (kBatchReads) {
         u32x4 kf[D / 16][NKB];
 #pragma unroll
@@ -450,12 +488,10 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
     };
 
     // ---- online softmax state (one query row per lane; lanes l and l^32 share a row)
-    // With a window, m_run stays -inf until the row sees a key; otherwise key 0 is visible
-    // to every row and the first tile always sets it.
-    float m_run = WINDOW ? -INFINITY : 0.f, l_run = 0.f;
-    // ALiBi: the score gets -slope_h * |i - j|, i.e. -beta * |i - j| in the units of the
-    // raw dot product that c = |scale| * log2(e) scales into exp2 units.
-    const float beta = ALIBI ? p.alibi[hq] * kLog2e / c : 0.f;
+    // With a window or nearest-first order, m_run stays -inf until the row sees a key;
+    // otherwise key 0 is visible to every row and the first tile always sets it.
+    constexpr bool kLateStart = WINDOW || kNearFirst;
+    float m_run = kLateStart ? -INFINITY : 0.f, l_run = 0.f;
 
     // Key j = t0 + 32kb + 8(i/4) + 4hh + (i%4) is kept iff lo <= j < lim: the signs of
     // j - lim and j - lo select between the score and the masked bit pattern (no compare
@@ -478,16 +514,15 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
       const int t0 = t * PF_BN;
       if (t0 + PF_BN > wave_mask_from || (WINDOW && t0 < wave_lo_hi)) mask(sc, t0);
     };
-    // ALiBi distance |i - j| of this lane's score (kb, i) in tile t: key j = t0 + 32kb +
-    // 8(i/4) + 4hh + (i%4), so i - j = dq(t) - (32kb + 8(i/4) + i%4).
+    // ALiBi distance |qa - j| of this lane's score (kb, i) in tile t: key j = t0 + 32kb +
+    // 8(i/4) + 4hh + (i%4), so qa - j = dq(t) - (32kb + 8(i/4) + i%4).
     // (The empty asm hides where dq came from, so the compiler recomputes the distances in
     // each use instead of keeping 32 of them live between the row max and the weights.)
     auto alibi_dq = [&](int t) {
-      float dq = (float)(qi - t * PF_BN - 4 * hh);
+      float dq = (float)(qa - t * PF_BN - 4 * hh);
       asm volatile("" : "+v"(dq));
       return dq;
     };
-    auto alibi_off = [](int kb, int i) { return (float)(32 * kb + 8 * (i >> 2) + (i & 3)); };
     // Row max of the (signed, biased) scores over the tile (the row's other keys sit in lane
     // l ^ 32).
     auto row_max = [&](const f32x16 (&sc)[NKB], int t) {
@@ -498,21 +533,39 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           float x = sc[kb][i] * sgn;
-          if constexpr (ALIBI) x = fmaf(-beta, fabsf(dq - alibi_off(kb, i)), x);
+          if constexpr (ALIBI && !kLinBias) x = fmaf(-beta, fabsf(dq - alibi_off(kb, i)), x);
           mx = fmaxf(mx, x);
         }
+      if constexpr (kLinBias) mx = fmaf(-beta, dq, mx);  // the per-tile bias term
       return pair_max(mx);
+    };
+    // A new exponent offset from tile t's scores: their row max, and with non-causal ALiBi
+    // that max raised by the tile's largest bias |i - j| * beta (capped at kLift exp2
+    // units). The tiles walk towards the diagonal and then away from it, and the lift keeps
+    // the nearer tiles under the offset, where the plain max of far, strongly biased keys
+    // would be passed by each of them. The cap keeps the tile's largest weight at or above
+    // 2^-kLift, so a row's weights never all underflow.
+    auto new_offset = [&](const f32x16 (&sc)[NKB], int t) {
+      float mx = row_max(sc, t);
+      if constexpr (ALIBI && !CAUSAL) {
+        constexpr float kLift = 64.f;
+        const float t0 = (float)(t * PF_BN), fq = (float)qa;
+        const float reach = fmaxf(fabsf(fq - t0), fabsf(fq - t0 - (float)(PF_BN - 1)));
+        mx += fminf(beta * reach, kLift / c);
+      }
+      return mx;
     };
     // Weights exp2(c sgn s - c m) rounded to bf16 as the PV operand; returns this lane's sum
     // of the rounded weights (the same values the PV product uses). exp2(-inf) = 0.
     auto weights = [&](const f32x16 (&sc)[NKB], bf16x8 (&pp)[NKS], int t) {
-      const float msc = ((WINDOW && m_run == -INFINITY) ? 0.f : m_run) * c;  // no key yet
+      const float msc = ((kLateStart && m_run == -INFINITY) ? 0.f : m_run) * c;  // no key yet
       const float dq = ALIBI ? alibi_dq(t) : 0.f;
       const float bc = beta * c;  // the bias slope in exp2 units
       // exp2 argument of score (kb, i): c * (sgn s - beta |i - j|) - c * m
+      const float base = kLinBias ? fmaf(-bc, dq, -msc) : -msc;
       auto arg = [&](int kb, int i) {
-        float x = fmaf(sc[kb][i], cs, -msc);
-        if constexpr (ALIBI) x = fmaf(-bc, fabsf(dq - alibi_off(kb, i)), x);
+        float x = fmaf(sc[kb][i], cs, base);
+        if constexpr (ALIBI && !kLinBias) x = fmaf(-bc, fabsf(dq - alibi_off(kb, i)), x);
         return x;
       };
       float lsum = 0.f;
@@ -545,13 +598,13 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
       qk(sc, kslot(u));
       issue(u + kAhead);
       prep(sc, t);
-      if constexpr (WINDOW) {
+      if constexpr (kLateStart) {
         if (wave_any(m_run == -INFINITY)) {  // rows that have not seen a key yet
-          const float mx = row_max(sc, t);
+          const float mx = new_offset(sc, t);
           if (m_run == -INFINITY) m_run = mx;  // stays -inf while all the row's keys are masked
         }
       } else if (t == 0) {
-        m_run = row_max(sc, t);  // key 0 is visible to every row, so this is finite
+        m_run = new_offset(sc, t);  // key 0 is visible to every row, so this is finite
       }
       bf16x8 pp[NKS];
       // The softmax runs at raised wave priority, so a SIMD prefers this wave's vector work
@@ -566,7 +619,7 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
         asm volatile("" ::: "memory");
         qk(sc, kslot(u));
         prep(sc, t);
-        const float m_new = fmaxf(m_run, row_max(sc, t));
+        const float m_new = fmaxf(m_run, new_offset(sc, t));
         const float alpha = m_new == m_run ? 1.f : fast_exp2((m_run - m_new) * c);
         l_run *= alpha;
 #pragma unroll
@@ -580,7 +633,8 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
       pv(pp, vslot(u));
     };
 
-    for (int t = t_first; t < ntiles; ++t, ++u) {
+    for (int n = t_first; n < ntiles; ++n, ++u) {
+      const int t = kNearFirst ? t_first + ntiles - 1 - n : n;  // key tile of position n
       if (t >= wave_t0 && t < wave_nt)
         tile(t, u);
       else
@@ -606,7 +660,8 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
         }
       if (p.lse && hh == 0)
         p.lse[((size_t)b * Hq + hq) * S + qi] =
-            l_tot > 0.f ? m_run * p.scale_abs + logf(l_tot) : -INFINITY;
+            l_tot > 0.f ? m_run * p.scale_abs + logf(l_tot) - slope * (float)(qi - qa)
+                        : -INFINITY;
     }
   }
   wait_vm<0>();  // drain the copies issued past the last tile

@@ -76,7 +76,14 @@ __global__ __launch_bounds__(PF32_THREADS) void prefill_f32_kernel(PrefillParams
       wave_lo_hi = min(fw + 31, R - 1) / g - p.window + 1;
     }
   }
-  const float beta = p.alibi ? p.alibi[hq] * kLog2e / p.scale_log2 : 0.f;
+  const float slope = p.alibi ? p.alibi[hq] : 0.f;
+  const float beta = slope * kLog2e / p.scale_log2;
+  // The bias is measured from key a = min(i, L_b - 1), the visible key nearest to the query:
+  // when i >= L_b every key lies below a, so |i - j| = |a - j| + (i - a). The constant
+  // slope * (i - a) drops out of the softmax and is added back to the LSE; without it, the
+  // scores of a row far past a short key range would all carry a large bias, and fp32 would
+  // resolve their differences only to the ulp of that bias.
+  const int qa = min(qi, Lb - 1);
 
   // B operand of S^T = K Q^T: lane holds Q[row][2*ks + hh].
   float qf[D / 2];
@@ -121,7 +128,7 @@ __global__ __launch_bounds__(PF32_THREADS) void prefill_f32_kernel(PrefillParams
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int j = t0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-        s[r] = fmaf(-beta, fabsf((float)(qi - j)), s[r]);
+        s[r] = fmaf(-beta, fabsf((float)(qa - j)), s[r]);
       }
     }
     const bool need_mask = t0 + PF32_BN > wave_mask_from || t0 < wave_lo_hi;
@@ -180,7 +187,7 @@ __global__ __launch_bounds__(PF32_THREADS) void prefill_f32_kernel(PrefillParams
       }
     if (p.lse && hh == 0)
       p.lse[((size_t)b * Hq + hq) * S + qi] =
-          l_tot > 0.f ? m_run * p.scale_abs + logf(l_tot) : -INFINITY;
+          l_tot > 0.f ? m_run * p.scale_abs + logf(l_tot) - slope * (float)(qi - qa) : -INFINITY;
   }
 }
 
