@@ -10,7 +10,8 @@ Independent anchors:
   * torch's float64 scaled_dot_product_attention with an explicit boolean mask
     (window) or an additive float mask (ALiBi), K/V heads expanded explicitly;
   * closed forms: window 1 (and a huge ALiBi slope) leaves only the diagonal key,
-    so O_i = V_i; zero slopes and windows >= S change nothing;
+    so O_i = V_i; past a key length L a huge slope leaves only key L - 1, whose biased
+    score is then the LSE; zero slopes and windows >= S change nothing;
   * gathering: a paged pool with the identity table, and with pages scattered
     by a random permutation, both equal the contiguous cache.
 A wrong window bound (off by one), a bias sign or scale error, a wrong bias
@@ -116,6 +117,23 @@ def test_alibi_huge_slope_keeps_the_diagonal(oracle_mod, causal):
     for i in range(S):
         for h in range(Hq):
             np.testing.assert_allclose(o[0, i, h], v[0, i, 0].numpy(), rtol=0, atol=1e-12)
+
+
+def test_alibi_huge_slope_lse_past_the_keys(oracle_mod):
+    """Rows at or past a short key length L with a huge slope: only the visible key nearest the
+    query survives, j* = min(i, L - 1), so O = v_j* and LSE = scale <q_i, k_j*> - slope |i - j*|
+    (the bias of every other key is smaller by at least the slope, e^-2000 of the total)."""
+    B, S, Hq, Hkv, d, L, slope, scale = 1, 10, 2, 1, 4, 4, 2000.0, 0.3
+    q, k, v = _rand((B, S, Hq, d), 71), _rand((B, S, Hkv, d), 72), _rand((B, S, Hkv, d), 73)
+    for causal in (False, True):
+        o, lse = oracle_mod.prefill(q, k, v, scale=scale, causal=causal, seqlens=[L],
+                                    alibi_slopes=[slope, slope])
+        for i in range(S):
+            js = min(i, L - 1)
+            for h in range(Hq):
+                s = scale * float(q[0, i, h] @ k[0, js, 0]) - slope * abs(i - js)
+                assert abs(lse[0, h, i] - s) < 1e-9 * max(1.0, abs(s))
+                np.testing.assert_allclose(o[0, i, h], v[0, js, 0].numpy(), rtol=0, atol=1e-12)
 
 
 def _decode_sdpa(q, kc, vc, lens, scale, window=0, slopes=None):
