@@ -106,10 +106,13 @@ int gqa_prefill_ex(int dtype, const void* q, const void* k, const void* v, void*
   p.window = window < S ? window : 0;  // a window of S or more keys hides nothing
   p.alibi = alibi_slopes;
   if (p.window > 0 && !causal) return GQA_ERR_UNSUPPORTED;
-  p.scale_abs = fabsf(softmax_scale);
   // A zero scale (uniform weights) still gets a positive exponent factor, tiny enough
   // that every valid weight rounds to exp2(0) = 1 while masked scores (-inf) give 0.
-  p.scale_log2 = fmaxf(p.scale_abs * kLog2e, kMinScaleLog2);
+  p.scale_log2 = fmaxf(fabsf(softmax_scale) * kLog2e, kMinScaleLog2);
+  // The LSE converts the kernels' running max (raw-score units) with the scale that factor
+  // stands for, not |softmax_scale|: with a zero scale and ALiBi the max holds a bias of
+  // slope / scale_log2 per key and must still come out as slope * distance.
+  p.scale_abs = p.scale_log2 / kLog2e;
   p.negate_q = softmax_scale < 0.f ? 1 : 0;
   p.rows_per_wg = dtype == GQA_DTYPE_BF16 ? gqa::prefill_rows_per_wg_bf16(d)
                                           : gqa::prefill_rows_per_wg_f32();
@@ -184,10 +187,13 @@ int gqa_decode_ex(int dtype, const void* q, const void* k_cache, const void* v_c
   p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_lse_offset);
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.g = Hq / Hkv; p.d = d; p.max_len = max_len;
   p.nqb = plan.nqb; p.n_units = plan.n_units; p.n_wg = plan.n_wg;
-  p.scale_abs = fabsf(softmax_scale);
   // A zero scale (uniform weights) still gets a positive exponent factor, tiny enough
   // that every valid weight rounds to exp2(0) = 1 while masked scores (-inf) give 0.
-  p.scale_log2 = fmaxf(p.scale_abs * kLog2e, kMinScaleLog2);
+  p.scale_log2 = fmaxf(fabsf(softmax_scale) * kLog2e, kMinScaleLog2);
+  // The LSE converts the kernels' running max (raw-score units) with the scale that factor
+  // stands for, not |softmax_scale|: with a zero scale and ALiBi the max holds a bias of
+  // slope / scale_log2 per key and must still come out as slope * distance.
+  p.scale_abs = p.scale_log2 / kLog2e;
   p.negate_q = softmax_scale < 0.f ? 1 : 0;
   p.window = window < max_len ? window : 0;  // a window of max_len or more keys hides nothing
   p.alibi = alibi_slopes;

@@ -17,8 +17,8 @@ struct PrefillParams {
   float* lse;
   const int32_t* seqlens;
   int B, S, Hq, Hkv, g, d;
-  float scale_log2;   // |softmax_scale| * log2(e)
-  float scale_abs;    // |softmax_scale|
+  float scale_log2;   // |softmax_scale| * log2(e), at least 1e-30
+  float scale_abs;    // scale_log2 / log2(e): |softmax_scale|, or the tiny stand-in for 0
   int negate_q;       // 1 when softmax_scale < 0 (the kernel negates q or the scores)
   int rows_per_wg;    // flattened rows per workgroup
   int nrb;            // row blocks per (b, kvh) unit

@@ -149,6 +149,52 @@ def test_prefill_alibi_steep_long(oracle_mod, dtype, d, Hkv, causal):
     assert e <= tol and le <= LSE_TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 64), (torch.bfloat16, 128),
+                                     (torch.float32, 64)])
+def test_prefill_zero_scale_with_alibi(oracle_mod, dtype, d):
+    """softmax_scale = 0 with ALiBi: the weights depend on the bias alone, which the kernels
+    carry in raw-score units (slope / exponent factor per key); O and the LSE must still
+    equal the oracle's, with rows past a short key length included."""
+    B, S, Hq, Hkv = 2, 200, 4, 2
+    _say(f"case prefill_ex zero scale + alibi {dtype} d={d}")
+    q, k, v = _rand((B, S, Hq, d), 2900 + d, dtype), _rand((B, S, Hkv, d), 2901 + d, dtype), \
+        _rand((B, S, Hkv, d), 2902 + d, dtype)
+    slopes = [0.5, 0.1, 2.0 ** -5, 2.0 ** -8]
+    lens = [200, 70]
+    ld = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    for causal in (True, False):
+        o, lse = gqa.prefill(q.cuda(), k.cuda(), v.cuda(), causal=causal, softmax_scale=0.0,
+                             seqlens=ld, alibi_slopes=slopes, return_lse=True)
+        torch.cuda.synchronize()
+        ro, rl = oracle_mod.prefill(q, k, v, scale=0.0, causal=causal, seqlens=lens,
+                                    alibi_slopes=slopes)
+        e, le = _errs(o, lse, ro, rl)
+        _say(f"  causal={causal} max_abs_err={e:.3e} lse_err={le:.3e}")
+        assert e <= TOL[dtype] and le <= LSE_TOL[dtype]
+
+
+def test_decode_zero_scale_with_alibi(oracle_mod):
+    """softmax_scale = 0 with ALiBi in the split-KV decode: a share that does not hold the
+    query's own key has its row max far below the other shares', and the merge weights the
+    shares by their LSEs, so a wrong LSE would show in O."""
+    B, Hq, Hkv, d, max_len = 3, 16, 2, 128, 1500
+    _say("case decode_ex zero scale + alibi")
+    q = _rand((B, Hq, d), 2950, torch.bfloat16)
+    kc = _rand((B, Hkv, max_len, d), 2951, torch.bfloat16)
+    vc = _rand((B, Hkv, max_len, d), 2952, torch.bfloat16)
+    lens = [1500, 700, 33]
+    slopes = [2.0 ** (-k / 2) for k in range(Hq)]
+    ref_o, ref_l = oracle_mod.decode(q, kc, vc, scale=0.0, lens=lens, alibi_slopes=slopes)
+    for splits in (0, 1, 5):
+        o, lse = gqa.decode(q.cuda(), kc.cuda(), vc.cuda(),
+                            torch.tensor(lens, dtype=torch.int32).cuda(), softmax_scale=0.0,
+                            num_splits=splits, alibi_slopes=slopes, return_lse=True)
+        torch.cuda.synchronize()
+        e, le = _errs(o, lse, ref_o, ref_l)
+        _say(f"  splits={splits} max_abs_err={e:.3e} lse_err={le:.3e}")
+        assert e <= 2e-2 and le <= DEC_LSE_TOL
+
+
 def test_prefill_window_full_size_sampled(oracle_mod):
     """Causal Llama-shaped prefill (B=4, S=4096, 32/8 heads, d=128) with a 1000-key window and
     ALiBi, in the launch configuration the benchmark uses; 300 sampled rows."""
