@@ -540,18 +540,19 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
       return pair_max(mx);
     };
     // A new exponent offset from tile t's scores: their row max, and with non-causal ALiBi
-    // that max raised by the tile's largest bias |i - j| * beta (capped at kLift exp2
-    // units). The tiles walk towards the diagonal and then away from it, and the lift keeps
-    // the nearer tiles under the offset, where the plain max of far, strongly biased keys
-    // would be passed by each of them. The cap keeps the tile's largest weight at or above
-    // 2^-kLift, so a row's weights never all underflow.
+    // that max raised by the tile's largest bias |i - j| * beta (at least 0, at most kLift
+    // exp2 units). The tiles walk towards the diagonal and then away from it, and the lift
+    // keeps the nearer tiles under the offset, where the plain max of far, strongly biased
+    // keys would be passed by each of them. The cap keeps the tile's largest weight at or
+    // above 2^-kLift, so a row's weights never all underflow; the floor keeps a negative
+    // slope from lowering the offset below the tile's own max.
     auto new_offset = [&](const f32x16 (&sc)[NKB], int t) {
       float mx = row_max(sc, t);
       if constexpr (ALIBI && !CAUSAL) {
         constexpr float kLift = 64.f;
         const float t0 = (float)(t * PF_BN), fq = (float)qa;
         const float reach = fmaxf(fabsf(fq - t0), fabsf(fq - t0 - (float)(PF_BN - 1)));
-        mx += fminf(beta * reach, kLift / c);
+        mx += fminf(fmaxf(beta * reach, 0.f), kLift / c);
       }
       return mx;
     };

@@ -151,6 +151,31 @@ def test_prefill_alibi_steep_long(oracle_mod, dtype, d, Hkv, causal):
 
 @pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 64), (torch.bfloat16, 128),
                                      (torch.float32, 64)])
+def test_prefill_negative_alibi_slopes(oracle_mod, dtype, d):
+    """Negative slopes (the bias grows with distance, up to +110 nats here, more than fp32's
+    exponent range in exp2 units): far keys can outweigh near ones, so every change of the
+    kernels' exponent offset goes the other way."""
+    B, S, Hq, Hkv = 2, 1100, 4, 2
+    _say(f"case prefill_ex negative alibi slopes {dtype} d={d}")
+    q, k, v = _rand((B, S, Hq, d), 2980 + d, dtype), _rand((B, S, Hkv, d), 2981 + d, dtype), \
+        _rand((B, S, Hkv, d), 2982 + d, dtype)
+    slopes = [-0.1, -0.01, 0.05, -2.0 ** -8]
+    lens = [1100, 333]
+    ld = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    for causal in (True, False):
+        o, lse = gqa.prefill(q.cuda(), k.cuda(), v.cuda(), causal=causal,
+                             softmax_scale=1 / math.sqrt(d), seqlens=ld, alibi_slopes=slopes,
+                             return_lse=True)
+        torch.cuda.synchronize()
+        ro, rl = oracle_mod.prefill(q, k, v, scale=1 / math.sqrt(d), causal=causal,
+                                    seqlens=lens, alibi_slopes=slopes)
+        e, le = _errs(o, lse, ro, rl)
+        _say(f"  causal={causal} max_abs_err={e:.3e} lse_err={le:.3e}")
+        assert e <= TOL[dtype] and le <= LSE_TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 64), (torch.bfloat16, 128),
+                                     (torch.float32, 64)])
 def test_prefill_zero_scale_with_alibi(oracle_mod, dtype, d):
     """softmax_scale = 0 with ALiBi: the weights depend on the bias alone, which the kernels
     carry in raw-score units (slope / exponent factor per key); O and the LSE must still
@@ -171,6 +196,26 @@ def test_prefill_zero_scale_with_alibi(oracle_mod, dtype, d):
         e, le = _errs(o, lse, ro, rl)
         _say(f"  causal={causal} max_abs_err={e:.3e} lse_err={le:.3e}")
         assert e <= TOL[dtype] and le <= LSE_TOL[dtype]
+
+
+def test_decode_negative_alibi_slopes(oracle_mod):
+    """Negative slopes in the split-KV decode: the oldest keys carry the largest bias."""
+    B, Hq, Hkv, d, max_len = 3, 8, 2, 64, 900
+    _say("case decode_ex negative alibi slopes")
+    q = _rand((B, Hq, d), 2990, torch.bfloat16)
+    kc = _rand((B, Hkv, max_len, d), 2991, torch.bfloat16)
+    vc = _rand((B, Hkv, max_len, d), 2992, torch.bfloat16)
+    lens = [900, 400, 17]
+    slopes = [-0.05, -0.01, 0.02, -2.0 ** -8, 0.0, -0.002, 0.1, -0.03]
+    ref_o, ref_l = oracle_mod.decode(q, kc, vc, scale=0.125, lens=lens, alibi_slopes=slopes)
+    for splits in (0, 1, 4):
+        o, lse = gqa.decode(q.cuda(), kc.cuda(), vc.cuda(),
+                            torch.tensor(lens, dtype=torch.int32).cuda(), softmax_scale=0.125,
+                            num_splits=splits, alibi_slopes=slopes, return_lse=True)
+        torch.cuda.synchronize()
+        e, le = _errs(o, lse, ref_o, ref_l)
+        _say(f"  splits={splits} max_abs_err={e:.3e} lse_err={le:.3e}")
+        assert e <= 2e-2 and le <= DEC_LSE_TOL
 
 
 def test_decode_zero_scale_with_alibi(oracle_mod):
