@@ -264,6 +264,26 @@ def test_decode_sweep(oracle_mod, d, Hq, Hkv):
             assert e <= 2e-2 and le <= BF16_DECODE_LSE_TOL
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_many_sequences(oracle_mod, d):
+    """1300 sequences (the split kernel scans lengths 512 at a time, the combine kernel 64 at a
+    time), lengths 0..200 with runs of empty caches: every share still finds its sequence."""
+    B, Hq, Hkv, max_len = 1300, 8, 2, 200
+    _say(f"case decode many sequences B={B} d={d}")
+    rng = np.random.default_rng(77 + d)
+    lens = rng.integers(0, max_len + 1, size=B)
+    lens[100:140] = 0
+    lens[-1] = max_len
+    lens = [int(x) for x in lens]
+    q = _rand((B, Hq, d), 4000 + d, torch.bfloat16)
+    kc = _rand((B, Hkv, max_len, d), 4001 + d, torch.bfloat16)
+    vc = _rand((B, Hkv, max_len, d), 4002 + d, torch.bfloat16)
+    for splits in (0, 1, 3):
+        e, le, _ = _run_decode_full(oracle_mod, q, kc, vc, lens, 0.1, splits)
+        _say(f"  splits={splits} max_abs_err={e:.3e} lse_err={le:.3e}")
+        assert e <= 2e-2 and le <= BF16_DECODE_LSE_TOL
+
+
 def test_decode_poisoned_cache_and_split_invariance(oracle_mod):
     """NaN/Inf past each length must not leak; every split count gives the oracle's answer."""
     B, Hq, Hkv, d, max_len = 5, 32, 1, 128, 2000
