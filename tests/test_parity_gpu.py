@@ -142,6 +142,48 @@ def test_prefill_many_ragged_sequences(oracle_mod, B, S, Hq, Hkv, d):
         assert e <= 2e-2 and le <= LSE_TOL[torch.bfloat16]
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefill_very_many_short_sequences(oracle_mod, d):
+    """1500 sequences of at most 24 keys: past the in-kernel length ranking (256 sequences),
+    thousands of work items for the persistent d = 128 workgroups."""
+    B, S, Hq, Hkv = 1500, 24, 4, 2
+    rng = np.random.default_rng(1500 + d)
+    lens = [int(x) for x in rng.integers(0, S + 1, size=B)]
+    q = _rand((B, S, Hq, d), 4100 + d, torch.bfloat16)
+    k = _rand((B, S, Hkv, d), 4101 + d, torch.bfloat16)
+    v = _rand((B, S, Hkv, d), 4102 + d, torch.bfloat16)
+    for causal in (False, True):
+        _say(f"case prefill B={B} S={S} d={d} causal={causal}")
+        e, le = _run_prefill_full(oracle_mod, q, k, v, lens, causal, 1 / math.sqrt(d),
+                                  torch.bfloat16)
+        _say(f"  max_abs_err={e:.3e} lse_err={le:.3e}")
+        assert e <= 2e-2 and le <= LSE_TOL[torch.bfloat16]
+
+
+@pytest.mark.parametrize("d,causal", [(64, False), (128, True)])
+def test_prefill_one_long_sequence_sampled(oracle_mod, d, causal):
+    """One 20000-key sequence (not a multiple of the tile) with a key length below it,
+    checked on sampled rows: long row loops and large offsets."""
+    B, S, Hq, Hkv = 1, 20000, 4, 1
+    lens = [19001]
+    _say(f"case prefill long S={S} d={d} causal={causal}")
+    q = _rand((B, S, Hq, d), 4200 + d, torch.bfloat16)
+    k = _rand((B, S, Hkv, d), 4201 + d, torch.bfloat16)
+    v = _rand((B, S, Hkv, d), 4202 + d, torch.bfloat16)
+    o, lse = gqa.prefill(q.cuda(), k.cuda(), v.cuda(), causal=causal,
+                         seqlens=torch.tensor(lens, dtype=torch.int32).cuda(), return_lse=True)
+    torch.cuda.synchronize()
+    rows = _sample_rows(B, S, Hq, torch.tensor(lens), 120, 11)
+    ref_o, ref_l = oracle_mod.prefill_rows(q, k, v, rows, scale=1 / math.sqrt(d), causal=causal,
+                                           seqlens=lens)
+    oc, lc = o.cpu(), lse.cpu()
+    got = torch.stack([oc[b, i, h] for b, h, i in rows])
+    got_l = torch.tensor([float(lc[b, h, i]) for b, h, i in rows], dtype=torch.float64)
+    e, le = _max_err(got, ref_o), _lse_err(got_l, ref_l)
+    _say(f"  rows={len(rows)} max_abs_err={e:.3e} lse_err={le:.3e}")
+    assert e <= 2e-2 and le <= LSE_TOL[torch.bfloat16]
+
+
 def test_prefill_poisoned_padding_does_not_leak(oracle_mod):
     """K/V rows at or past a sequence's length hold NaN/Inf: the output must not see them."""
     B, S, Hq, Hkv, d = 3, 150, 8, 2, 128
