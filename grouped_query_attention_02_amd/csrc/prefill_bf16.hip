@@ -29,7 +29,10 @@
 //
 // Masks: key j is visible to query i iff j < L_b and (not causal or j <= i). K/V rows
 // at or past L_b are never read (they arrive in LDS as zeros), so padding may hold
-// anything.
+// anything. Options (template flags, so the plain kernels carry none of their code): a
+// causal sliding window (keys j > i - w; tiles below every row's window are skipped) and
+// ALiBi (score - slope_h |i - j|). Causal ALiBi visits each item's tiles from the diagonal
+// down, with the bias folded into the accumulators and the exponent offset.
 #include "gqa_device.h"
 #include "gqa_kernels.h"
 
@@ -588,12 +591,13 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
       return lsum;
     };
 
-    // The exponent offset m_run is the row max of the first tile in which the row sees a
-    // key, and stays fixed while every weight of a tile is at most 2^32 (checked through the
-    // tile's weight sum, which bounds each weight). A tile that breaks this (scores grown
-    // past the offset) is redone with the offset raised to its row max, after rescaling what
-    // was accumulated. Every term of a row always shares one offset, so the normalised
-    // result is that of the exact max.
+    // The exponent offset m_run comes from the first tile in which the row sees a key
+    // (new_offset: its row max, lifted for non-causal ALiBi), and stays fixed while every
+    // weight of a tile is at most 2^32 (checked through the tile's weight sum, which bounds
+    // each weight). A tile that breaks this (scores grown past the offset) is redone with
+    // the offset raised to at least its row max, after rescaling what was accumulated.
+    // Every term of a row always shares one offset, so the normalised result is that of
+    // the exact max.
     auto tile = [&](int t, int u) {
       f32x16 sc[NKB];
       qk(sc, kslot(u));
