@@ -355,8 +355,9 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_split_kernel(DecodeParam
       if (more) load_v(r, tt + DC_WAVES);  // V registers are free again
     };
 
-    // The wave's tiles are ta + wave, ta + wave + 4, ...; each tile's K (V) registers are
-    // refilled with the next tile's rows as soon as QK^T (PV) has consumed them.
+    // The wave's tiles are ta + wave, ta + wave + DC_WAVES, ...; each tile's K (V)
+    // registers are refilled with the next tile's rows as soon as QK^T (PV) has consumed
+    // them.
     for (int tt = ta + wave; tt < te; tt += DC_WAVES) compute_tile(r0, tt, tt + DC_WAVES < te);
 
     // Merge the waves' running states through LDS.
