@@ -182,12 +182,15 @@ def _extended_rows(steps, dev):
 
 
 def _cpu_baseline(pc, target_s: float):
-    """The fp64 oracle, as it stands, on a random row sample of the prefill workload."""
+    """The fp64 oracle, as it stands, on random rows of the prefill workload: a 2000-row pilot
+    sizes the sample to about target_s seconds, run in chunks of at most one workload's worth
+    of rows (drawn with replacement, so a fast host may see each row more than once)."""
     import numpy as np
     import oracle
     w = pc["w"]
     x = pc["host"]
     lens = x["seqlens"].numpy() if x["seqlens"] is not None else np.full(w.B, w.S)
+    lens = np.asarray(lens, dtype=np.int64)
     rng = np.random.default_rng(0)
 
     def sample(n):
@@ -195,25 +198,31 @@ def _cpu_baseline(pc, target_s: float):
                          rng.integers(w.S, size=n)], 1).astype(np.int64)
 
     def flops(rows):
-        return sum(4 * w.d * (min(int(i) + 1, int(lens[b])) if w.causal else int(lens[b]))
-                   for b, h, i in rows)
+        keys = lens[rows[:, 0]]
+        if w.causal:
+            keys = np.minimum(rows[:, 2] + 1, keys)
+        return 4.0 * w.d * float(keys.sum())
+
+    def run(rows):
+        t = time.perf_counter()
+        oracle.prefill_rows(x["q"], x["k"], x["v"], rows, scale=w.softmax_scale,
+                            causal=w.causal, seqlens=x["seqlens"])
+        return time.perf_counter() - t
 
     pilot = sample(2000)
-    t = time.perf_counter()
-    oracle.prefill_rows(x["q"], x["k"], x["v"], pilot, scale=w.softmax_scale, causal=w.causal,
-                        seqlens=x["seqlens"])
-    rate = flops(pilot) / max(time.perf_counter() - t, 1e-6)
+    rate = flops(pilot) / max(run(pilot), 1e-6)
     total_rows = w.B * w.S * w.Hq
-    n = int(min(total_rows, max(2000, rate * target_s / (4 * w.d * float(np.mean(lens))))))
-    rows = sample(n)
-    t = time.perf_counter()
-    oracle.prefill_rows(x["q"], x["k"], x["v"], rows, scale=w.softmax_scale, causal=w.causal,
-                        seqlens=x["seqlens"])
-    dt = time.perf_counter() - t
-    return {"value": flops(rows) / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
+    goal = int(max(2000, rate * target_s / (4 * w.d * float(np.mean(lens)))))
+    done, fl, dt = 0, 0.0, 0.0
+    while done < goal:
+        rows = sample(min(total_rows, goal - done))
+        dt += run(rows)
+        fl += flops(rows)
+        done += len(rows)
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
             "kind": "oracle",
-            "sample": f"{n} random (b, head, query) rows of {w.name} ({n / total_rows:.1%} of "
-                      f"its {total_rows} rows), fp64, {dt:.1f} s wall"}
+            "sample": f"{done} random (b, head, query) rows of {w.name}, drawn with replacement "
+                      f"({done / total_rows:.2f} x its {total_rows} rows), fp64, {dt:.1f} s wall"}
 
 
 def _only(what, steps, dev):
@@ -370,7 +379,7 @@ def main(argv=None):
     ap.add_argument("--no-extra", action="store_true", help="skip the extra workloads")
     ap.add_argument("--no-probes", action="store_true",
                     help="skip the achievable-peak microbenchmarks (achievable = null)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", choices=["prefill", "decode", "copy"],
                     help="profiling run: execute just this work --steps times and exit")
     ap.add_argument("--summarize-kernels", metavar="DIR",
