@@ -13,7 +13,7 @@ and reported under `also` (not part of `value`), and two microbenchmarks give th
 this GPU reaches (`achievable`: bf16 MFMA loop, streaming HBM read).
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra] [--no-probes]
-    python bench.py --only prefill|decode|copy --steps K     (work for rocprofv3 runs)
+    python bench.py --only prefill|prefill_causal|decode|copy --steps K   (work for rocprofv3 runs)
     python bench.py --summarize-kernels DIR | --summarize-pmc DIR
 """
 from __future__ import annotations
@@ -229,8 +229,9 @@ def _only(what, steps, dev):
     """Run one piece of work `steps` times (for rocprofv3 runs) and exit."""
     import torch
     import workloads as W
-    if what == "prefill":
-        c = _prefill_case(W.WORKLOADS["bert_base_prefill"], dev)
+    if what in ("prefill", "prefill_causal"):
+        name = "bert_base_prefill" if what == "prefill" else "llama_causal_prefill"
+        c = _prefill_case(W.WORKLOADS[name], dev)
         fn = lambda: _run_prefill(c)
     elif what == "decode":
         c = _decode_case(W.WORKLOADS["mqa_ragged_decode"], dev)
@@ -380,7 +381,7 @@ def main(argv=None):
     ap.add_argument("--no-probes", action="store_true",
                     help="skip the achievable-peak microbenchmarks (achievable = null)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--only", choices=["prefill", "decode", "copy"],
+    ap.add_argument("--only", choices=["prefill", "prefill_causal", "decode", "copy"],
                     help="profiling run: execute just this work --steps times and exit")
     ap.add_argument("--summarize-kernels", metavar="DIR",
                     help="print per-kernel mean durations from rocprofv3 --kernel-trace CSV output")
