@@ -13,7 +13,9 @@ Independent anchors:
     so O_i = V_i; past a key length L a huge slope leaves only key L - 1, whose biased
     score is then the LSE; zero slopes and windows >= S change nothing;
   * gathering: a paged pool with the identity table, and with pages scattered
-    by a random permutation, both equal the contiguous cache.
+    by a random permutation, both equal the contiguous cache;
+  * the sampled entry points (prefill_rows, decode_pairs) that the full-size GPU
+    tests use equal the whole computation at the same rows and pairs.
 A wrong window bound (off by one), a bias sign or scale error, a wrong bias
 position for decode, or a wrong page/row split fails at least one test.
 """
@@ -225,3 +227,45 @@ def test_paged_cache_rejects_a_bad_page(oracle_mod):
         oracle_mod.decode(q, kp, vp, scale=1.0, lens=[8], block_table=table, page_size=P)
     # a bad entry past the sequence's length is never looked at
     oracle_mod.decode(q, kp, vp, scale=1.0, lens=[4], block_table=table, page_size=P)
+
+
+@pytest.mark.parametrize("causal,window,with_alibi", [(False, 0, False), (True, 0, False),
+                                                      (True, 5, True), (False, 0, True)])
+def test_sampled_rows_equal_the_whole_prefill(oracle_mod, causal, window, with_alibi):
+    """prefill_rows (the full-size GPU tests' reference) gives, row for row, what the whole
+    prefill gives: same indexing of (b, h, i), same masks and bias."""
+    B, S, Hq, Hkv, d = 2, 13, 6, 2, 8
+    q, k, v = _rand((B, S, Hq, d), 81), _rand((B, S, Hkv, d), 82), _rand((B, S, Hkv, d), 83)
+    lens = [13, 7]
+    slopes = [0.3, 0.1, 0.05, 0.7, 0.0, 1.2] if with_alibi else None
+    o, lse = oracle_mod.prefill(q, k, v, scale=0.4, causal=causal, seqlens=lens, window=window,
+                                alibi_slopes=slopes)
+    rng = np.random.default_rng(5)
+    rows = np.stack([rng.integers(B, size=40), rng.integers(Hq, size=40),
+                     rng.integers(S, size=40)], 1)
+    ro, rl = oracle_mod.prefill_rows(q, k, v, rows, scale=0.4, causal=causal, seqlens=lens,
+                                     window=window, alibi_slopes=slopes)
+    for r, (b, h, i) in enumerate(rows):
+        np.testing.assert_allclose(ro[r], o[b, i, h], rtol=0, atol=1e-13)
+        if np.isfinite(lse[b, h, i]):
+            assert abs(rl[r] - lse[b, h, i]) < 1e-13
+        else:
+            assert rl[r] == lse[b, h, i]
+
+
+@pytest.mark.parametrize("window,with_alibi", [(0, False), (4, True)])
+def test_sampled_pairs_equal_the_whole_decode(oracle_mod, window, with_alibi):
+    """decode_pairs gives, pair for pair, what the whole decode gives."""
+    B, Hq, Hkv, d, max_len = 3, 6, 3, 8, 20
+    q = _rand((B, Hq, d), 91)
+    kc, vc = _rand((B, Hkv, max_len, d), 92), _rand((B, Hkv, max_len, d), 93)
+    lens = [20, 1, 9]
+    slopes = [0.2, 0.0, 0.6, 0.1, 1.0, 0.03] if with_alibi else None
+    o, lse = oracle_mod.decode(q, kc, vc, scale=0.3, lens=lens, window=window,
+                               alibi_slopes=slopes)
+    pairs = [(b, h) for b in range(B) for h in range(Hq)]
+    po, pl = oracle_mod.decode_pairs(q, kc, vc, pairs, scale=0.3, lens=lens, window=window,
+                                     alibi_slopes=slopes)
+    for r, (b, h) in enumerate(pairs):
+        np.testing.assert_allclose(po[r], o[b, h], rtol=0, atol=1e-13)
+        assert abs(pl[r] - lse[b, h]) < 1e-13
