@@ -253,14 +253,18 @@ def test_prefill_gqa_equals_replicated_mha():
         assert (a.float() - b.float()).abs().max().item() <= 2e-2
 
 
-def test_prefill_deterministic():
-    B, S, Hq, Hkv, d = 2, 300, 32, 8, 128
+@pytest.mark.parametrize("d,causal", [(128, True), (64, False)])
+def test_prefill_deterministic(d, causal):
+    """Bitwise-equal outputs over 10 runs: the persistent d = 128 kernel and the d = 64 kernel
+    with in-kernel length ranking."""
+    B, S, Hq, Hkv = 4, 300, 32, 8
     q = _rand((B, S, Hq, d), 41, torch.bfloat16).cuda()
     k = _rand((B, S, Hkv, d), 42, torch.bfloat16).cuda()
     v = _rand((B, S, Hkv, d), 43, torch.bfloat16).cuda()
-    first = gqa.prefill(q, k, v, causal=True)
-    for _ in range(5):
-        assert torch.equal(gqa.prefill(q, k, v, causal=True), first)
+    lens = torch.tensor([300, 17, 250, 129], dtype=torch.int32).cuda()
+    first = gqa.prefill(q, k, v, causal=causal, seqlens=lens)
+    for _ in range(10):
+        assert torch.equal(gqa.prefill(q, k, v, causal=causal, seqlens=lens), first)
 
 
 def test_prefill_v_ones_gives_ones():
@@ -378,7 +382,7 @@ def test_decode_deterministic():
     vc = _rand((B, Hkv, max_len, d), 93, torch.bfloat16).cuda()
     lens = torch.tensor([5000, 3, 4000, 100, 2500, 1, 4999, 64], dtype=torch.int32).cuda()
     first = gqa.decode(q, kc, vc, lens)
-    for _ in range(5):
+    for _ in range(10):
         assert torch.equal(gqa.decode(q, kc, vc, lens), first)
 
 

@@ -395,3 +395,82 @@ def test_bad_page_ids_read_as_zeros():
     torch.cuda.synchronize()
     assert torch.isfinite(o.float()).all()
     assert (o.float() - ref.float()).abs().max().item() <= 2e-2
+
+
+def _random_prefill_case(rng):
+    d = int(rng.choice([32, 64, 128]))
+    g = int(rng.choice([1, 2, 4, 8, 32]))
+    Hkv = int(rng.integers(1, 4)) if g < 32 else 1
+    S = int(rng.integers(1, 260 if g < 32 else 140))
+    B = int(rng.integers(1, 6))
+    causal = bool(rng.integers(2))
+    lens = [int(x) for x in rng.integers(0, S + 3, size=B)] if rng.integers(3) else None
+    window = int(rng.integers(1, S + 2)) if causal and rng.integers(2) else 0
+    slopes = list(rng.uniform(0.0, 0.5, size=g * Hkv)) if rng.integers(2) else None
+    dtype = torch.float32 if rng.integers(4) == 0 else torch.bfloat16
+    scale = float(rng.choice([1 / math.sqrt(d), 0.3, -0.2]))
+    return dict(d=d, Hq=g * Hkv, Hkv=Hkv, S=S, B=B, causal=causal, lens=lens, window=window,
+                slopes=slopes, dtype=dtype, scale=scale)
+
+
+@pytest.mark.parametrize("case_seed", range(30))
+def test_prefill_random_shapes(oracle_mod, case_seed):
+    """Seeded random configurations across head size, group size (1-32), length (from 1),
+    batch, key lengths (with zeros and clamped values), causal, window, ALiBi, dtype and scale."""
+    c = _random_prefill_case(np.random.default_rng(7000 + case_seed))
+    _say(f"case prefill random #{case_seed}: {c}")
+    B, S, Hq, Hkv, d = c["B"], c["S"], c["Hq"], c["Hkv"], c["d"]
+    q = _rand((B, S, Hq, d), 7100 + case_seed, c["dtype"])
+    k = _rand((B, S, Hkv, d), 7200 + case_seed, c["dtype"])
+    v = _rand((B, S, Hkv, d), 7300 + case_seed, c["dtype"])
+    ld = None if c["lens"] is None else torch.tensor(c["lens"], dtype=torch.int32, device="cuda")
+    o, lse = gqa.prefill(q.cuda(), k.cuda(), v.cuda(), causal=c["causal"], softmax_scale=c["scale"],
+                         seqlens=ld, window=c["window"], alibi_slopes=c["slopes"],
+                         return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle_mod.prefill(q, k, v, scale=c["scale"], causal=c["causal"], seqlens=c["lens"],
+                                window=c["window"], alibi_slopes=c["slopes"])
+    e, le = _errs(o, lse, ro, rl)
+    _say(f"  max_abs_err={e:.3e} lse_err={le:.3e}")
+    assert e <= TOL[c["dtype"]] and le <= LSE_TOL[c["dtype"]]
+
+
+@pytest.mark.parametrize("case_seed", range(20))
+def test_decode_random_shapes(oracle_mod, case_seed):
+    """Seeded random decode configurations: head size, group size (1-64), cache length,
+    batch, lengths (with zeros), window, ALiBi, paged or contiguous, split count and scale."""
+    rng = np.random.default_rng(8000 + case_seed)
+    d = int(rng.choice([64, 128]))
+    g = int(rng.choice([1, 2, 4, 8, 32, 40, 64]))
+    Hkv = int(rng.integers(1, 4))
+    page = int(rng.choice([0, 32, 64, 256]))
+    max_len = int(rng.integers(1, 900))
+    if page:
+        max_len = -(-max_len // page) * page
+    B = int(rng.integers(1, 7))
+    lens = [int(x) for x in rng.integers(0, max_len + 1, size=B)]
+    window = int(rng.integers(1, max_len + 2)) if rng.integers(2) else 0
+    slopes = list(rng.uniform(0.0, 0.5, size=g * Hkv)) if rng.integers(2) else None
+    splits = int(rng.choice([0, 1, 2, 7]))
+    scale = float(rng.choice([1 / math.sqrt(d), 0.25, -0.1]))
+    Hq = g * Hkv
+    _say(f"case decode random #{case_seed}: d={d} Hq={Hq} Hkv={Hkv} max_len={max_len} B={B} "
+         f"lens={lens} window={window} alibi={slopes is not None} page={page} splits={splits} "
+         f"scale={scale:.3f}")
+    q = _rand((B, Hq, d), 8100 + case_seed, torch.bfloat16)
+    kc = _rand((B, Hkv, max_len, d), 8200 + case_seed, torch.bfloat16)
+    vc = _rand((B, Hkv, max_len, d), 8300 + case_seed, torch.bfloat16)
+    if page:
+        kp, vp, table = _paged(kc, vc, page, 8400 + case_seed)
+        kd, vd, args = kp.cuda(), vp.cuda(), dict(block_table=table.cuda(), page_size=page)
+    else:
+        kd, vd, args = kc.cuda(), vc.cuda(), {}
+    o, lse = gqa.decode(q.cuda(), kd, vd, torch.tensor(lens, dtype=torch.int32).cuda(),
+                        softmax_scale=scale, num_splits=splits, window=window,
+                        alibi_slopes=slopes, return_lse=True, **args)
+    torch.cuda.synchronize()
+    ro, rl = oracle_mod.decode(q, kc, vc, scale=scale, lens=lens, window=window,
+                               alibi_slopes=slopes)
+    e, le = _errs(o, lse, ro, rl)
+    _say(f"  max_abs_err={e:.3e} lse_err={le:.3e}")
+    assert e <= 2e-2 and le <= DEC_LSE_TOL
