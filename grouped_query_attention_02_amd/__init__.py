@@ -50,6 +50,35 @@ def _check(t, name, ndim, dtype=None):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _check_buffer(t, name, shape, dtype, device):
+    """A caller-provided output buffer: the kernels write every element of `shape`
+    unconditionally, so anything smaller, of another type or elsewhere is rejected before
+    any launch."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_workspace(ws, need, device):
+    torch = _torch()
+    if not isinstance(ws, torch.Tensor):
+        raise TypeError("workspace must be a torch tensor")
+    if not ws.is_cuda or ws.device != device:
+        raise ValueError(f"workspace must be on {device}, got {ws.device}")
+    if ws.dtype != torch.uint8 or ws.dim() != 1 or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous 1-D uint8 tensor")
+    if ws.numel() < need:
+        raise ValueError(f"workspace holds {ws.numel()} bytes; this call needs {need}")
+
+
 def _lens_arg(x, B, device, name):
     torch = _torch()
     if x is None:
@@ -99,6 +128,8 @@ def prefill(q, k, v, *, causal: bool = False, softmax_scale: Optional[float] = N
     _check(q, "q", 4)
     _check(k, "k", 4, q.dtype)
     _check(v, "v", 4, q.dtype)
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k and v must be on the same device")
     B, S, Hq, d = q.shape
     Hkv = k.shape[2]
     if tuple(k.shape) != (B, S, Hkv, d) or tuple(v.shape) != tuple(k.shape):
@@ -109,14 +140,16 @@ def prefill(q, k, v, *, causal: bool = False, softmax_scale: Optional[float] = N
     if out is None:
         out = torch.empty_like(q)
     else:
-        _check(out, "out", 4, q.dtype)
+        _check_buffer(out, "out", q.shape, q.dtype, q.device)
     lse_ptr = 0
     if return_lse:
         if lse_out is None:
             lse_out = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
         else:
-            _check(lse_out, "lse_out", 3, torch.float32)
+            _check_buffer(lse_out, "lse_out", (B, Hq, S), torch.float32, q.device)
         lse_ptr = lse_out.data_ptr()
+    elif lse_out is not None:
+        raise ValueError("lse_out is given but return_lse is False")
     lens, lens_ptr = _lens_arg(seqlens, B, q.device, "seqlens")
     slopes, slopes_ptr = _slopes_arg(alibi_slopes, Hq, q.device)
     st = load().gqa_prefill_ex(_dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(),
@@ -155,6 +188,8 @@ def decode(q, k_cache, v_cache, cache_lens=None, *, softmax_scale: Optional[floa
     _check(q, "q", 3)
     _check(k_cache, "k_cache", 4, q.dtype)
     _check(v_cache, "v_cache", 4, q.dtype)
+    if k_cache.device != q.device or v_cache.device != q.device:
+        raise ValueError("q, k_cache and v_cache must be on the same device")
     B, Hq, d = q.shape
     Hkv = k_cache.shape[1]
     if tuple(v_cache.shape) != tuple(k_cache.shape) or k_cache.shape[3] != d:
@@ -166,6 +201,8 @@ def decode(q, k_cache, v_cache, cache_lens=None, *, softmax_scale: Optional[floa
             raise ValueError("k_cache and v_cache must be [B, Hkv, max_len, d]")
     else:
         _check(block_table, "block_table", 2, torch.int32)
+        if block_table.device != q.device:
+            raise ValueError("block_table must be on q's device")
         if block_table.shape[0] != B or k_cache.shape[2] != page_size:
             raise ValueError("paged cache: pools [num_pages, Hkv, page_size, d], "
                              "block_table [B, max_blocks]")
@@ -178,15 +215,21 @@ def decode(q, k_cache, v_cache, cache_lens=None, *, softmax_scale: Optional[floa
     need = decode_workspace_bytes(B, Hq, Hkv, d, max_len, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    else:
+        _check_workspace(workspace, need, q.device)
     if out is None:
         out = torch.empty_like(q)
     else:
-        _check(out, "out", 3, q.dtype)
+        _check_buffer(out, "out", q.shape, q.dtype, q.device)
     lse_ptr = 0
     if return_lse:
         if lse_out is None:
             lse_out = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+        else:
+            _check_buffer(lse_out, "lse_out", (B, Hq), torch.float32, q.device)
         lse_ptr = lse_out.data_ptr()
+    elif lse_out is not None:
+        raise ValueError("lse_out is given but return_lse is False")
     lens, lens_ptr = _lens_arg(cache_lens, B, q.device, "cache_lens")
     slopes, slopes_ptr = _slopes_arg(alibi_slopes, Hq, q.device)
     st = load().gqa_decode_ex(_dtype_code(q), q.data_ptr(), k_cache.data_ptr(),
@@ -212,9 +255,8 @@ def mean_pool_heads(w, num_groups: int, *, out=None):
     per_head = w.numel() // H if H else 0
     if out is None:
         out = torch.empty((num_groups,) + tuple(w.shape[1:]), dtype=w.dtype, device=w.device)
-    elif tuple(out.shape) != (num_groups,) + tuple(w.shape[1:]) or out.dtype != w.dtype \
-            or not out.is_contiguous():
-        raise ValueError("out must be a contiguous [num_groups, ...] tensor of w's dtype")
+    else:
+        _check_buffer(out, "out", (num_groups,) + tuple(w.shape[1:]), w.dtype, w.device)
     st = load().gqa_mean_pool_heads(_dtype_code(w), w.data_ptr(), H, int(num_groups), per_head,
                                     out.data_ptr(), _stream_ptr(w.device))
     if st != GQA_OK:

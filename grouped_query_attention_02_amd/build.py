@@ -70,6 +70,45 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host-side sanitizers for the library's host code (argument checks, planning, launch
+# set-up): each flag sits right after -Xarch_host, so the device code is built as usual.
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host",
+                 "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+
+
+def clang_asan_runtime():
+    """Path of the ASan runtime of the compiler hipcc drives (None if not installed)."""
+    r = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    path = r.stdout.strip().splitlines()[-1] if r.stdout.strip() else ""
+    if os.path.isabs(path) and os.path.exists(path):
+        return path
+    import glob
+    hits = sorted(glob.glob("/opt/rocm*/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return hits[-1] if hits else None
+
+
+def build_host_sanitized(path: str) -> str:
+    """libgqa.so with ASan + UBSan on its host code, written to `path` (for the CPU tests of
+    the C ABI; the process must load the ASan runtime first)."""
+    bdir = os.path.join(os.path.dirname(path), "objs")
+    os.makedirs(bdir, exist_ok=True)
+    objs = []
+    for src in sources():
+        obj = os.path.join(bdir, os.path.basename(src)[:-4] + ".o")
+        r = subprocess.run([HIPCC, *CFLAGS, *HOST_SANITIZE, "-c", src, "-o", obj],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
+        objs.append(obj)
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *HOST_SANITIZE,
+                        "-shared-libsan", "-o", path, *objs], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    return path
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)

@@ -525,9 +525,13 @@ hipError_t launch_d(const DecodeParams& p, bool need_combine, hipStream_t stream
   const size_t lds = Lay::Q_BYTES + (Lay::O_FLOATS + 2 * DC_WAVES * 32) * sizeof(float) +
                      (DC_WAVES + 4) * sizeof(long long);
   auto kern = decode_split_kernel<D, ALIBI, PAGED>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  static KernelSetup setup;  // per device: LDS attribute set
+  int dev = 0, cus = 0, per_cu = 1;
+  hipError_t e = current_device(&dev, &cus);
   if (e != hipSuccess) return e;
+  if ((e = setup_kernel(setup, reinterpret_cast<const void*>(kern), DC_THREADS, lds, dev,
+                        &per_cu)) != hipSuccess)
+    return e;
   hipLaunchKernelGGL(kern, dim3(p.n_wg), dim3(DC_THREADS), lds, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess || !need_combine) return e;

@@ -62,6 +62,120 @@ bool plan_decode(int B, int Hq, int Hkv, int d, int max_len, int num_splits, Dec
 
 }  // namespace
 
+namespace gqa {
+
+hipError_t current_device(int* dev_out, int* cus_out) {
+  static int cus_cache[kMaxDevices];  // 0 = not queried yet
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  *dev_out = dev;
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  if (cached) {
+    const int c = __atomic_load_n(&cus_cache[dev], __ATOMIC_ACQUIRE);
+    if (c > 0) {
+      *cus_out = c;
+      return hipSuccess;
+    }
+  }
+  int c = 0;
+  if ((e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+    return e;
+  if (c <= 0) c = 1;
+  // Two threads racing here store the same value.
+  if (cached) __atomic_store_n(&cus_cache[dev], c, __ATOMIC_RELEASE);
+  *cus_out = c;
+  return hipSuccess;
+}
+
+hipError_t setup_kernel(KernelSetup& s, const void* kern, int threads, size_t lds, int dev,
+                        int* per_cu_out) {
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  if (cached) {
+    const int v = __atomic_load_n(&s.per_cu[dev], __ATOMIC_ACQUIRE);
+    if (v > 0) {
+      *per_cu_out = v;
+      return hipSuccess;
+    }
+  }
+  hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  int nb = 0;
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, threads, lds)) != hipSuccess)
+    return e;
+  if (nb <= 0) nb = 1;
+  if (cached) __atomic_store_n(&s.per_cu[dev], nb, __ATOMIC_RELEASE);
+  *per_cu_out = nb;
+  return hipSuccess;
+}
+
+}  // namespace gqa
+
+namespace {
+
+// Every argument check of a decode call except the workspace's (host only, no HIP call).
+int check_decode(int dtype, const void* q, const void* k_cache, const void* v_cache,
+                 const int32_t* cache_lens, const int32_t* block_table, int page_size,
+                 int max_blocks, int num_pages, const void* o, const float* lse, int B, int Hq,
+                 int Hkv, int d, int max_len, float softmax_scale, int window,
+                 const float* alibi_slopes, int num_splits, DecodePlan* plan) {
+  if (!plan_decode(B, Hq, Hkv, d > 0 ? d : 1, max_len, num_splits, plan))
+    return GQA_ERR_INVALID_ARG;
+  if (!q || !k_cache || !v_cache || !o) return GQA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return GQA_ERR_INVALID_ARG;
+  if ((lse && ((uintptr_t)lse & 3u)) || (cache_lens && ((uintptr_t)cache_lens & 3u)) ||
+      (alibi_slopes && ((uintptr_t)alibi_slopes & 3u)) ||
+      (block_table && ((uintptr_t)block_table & 3u)))
+    return GQA_ERR_INVALID_ARG;
+  if (!isfinite(softmax_scale) || window < 0) return GQA_ERR_INVALID_ARG;
+  if (block_table) {
+    // Paged cache: tiles of 32 keys must not straddle pages, and the table covers max_len.
+    if (page_size <= 0 || page_size % kDecodeTile != 0 || max_blocks <= 0 || num_pages <= 0 ||
+        (long long)page_size * max_blocks != max_len)
+      return GQA_ERR_INVALID_ARG;
+  }
+  if (dtype != GQA_DTYPE_BF16) return GQA_ERR_UNSUPPORTED;
+  if (!supported_decode_d(d)) return GQA_ERR_UNSUPPORTED;
+  return GQA_OK;
+}
+
+// Launch of a checked decode call; `workspace` holds at least plan.ws_bytes bytes.
+int launch_decode(const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* cache_lens, const int32_t* block_table, int page_size,
+                  int max_blocks, int num_pages, void* o, float* lse, int B, int Hq, int Hkv,
+                  int d, int max_len, float softmax_scale, int window,
+                  const float* alibi_slopes, const DecodePlan& plan, void* workspace,
+                  void* stream) {
+  gqa::DecodeParams p;
+  p.q = q; p.kc = k_cache; p.vc = v_cache; p.lens = cache_lens; p.o = o; p.lse = lse;
+  p.ws_o = static_cast<float*>(workspace);
+  p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_lse_offset);
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.g = Hq / Hkv; p.d = d; p.max_len = max_len;
+  p.nqb = plan.nqb; p.n_units = plan.n_units; p.n_wg = plan.n_wg;
+  // A zero scale (uniform weights) still gets a positive exponent factor, tiny enough
+  // that every valid weight rounds to exp2(0) = 1 while masked scores (-inf) give 0.
+  p.scale_log2 = fmaxf(fabsf(softmax_scale) * kLog2e, kMinScaleLog2);
+  // The LSE converts the kernels' running max (raw-score units) with the scale that factor
+  // stands for, not |softmax_scale|: with a zero scale and ALiBi the max holds a bias of
+  // slope / scale_log2 per key and must still come out as slope * distance.
+  p.scale_abs = p.scale_log2 / kLog2e;
+  p.negate_q = softmax_scale < 0.f ? 1 : 0;
+  p.window = window < max_len ? window : 0;  // a window of max_len or more keys hides nothing
+  p.alibi = alibi_slopes;
+  p.block_table = block_table;
+  p.page_size = block_table ? page_size : 0;
+  p.max_blocks = block_table ? max_blocks : 0;
+  p.num_pages = block_table ? num_pages : 0;
+  // With no length array every unit has the same tile count; one share per unit then
+  // maps each workgroup onto exactly one whole unit and no merge pass is needed.
+  const bool need_combine = !(cache_lens == nullptr && plan.n_wg == plan.n_units);
+  hipError_t e = gqa::launch_decode_bf16(p, need_combine, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+}  // namespace
+
 extern "C" {
 
 int gqa_version(void) { return kVersion; }
@@ -160,52 +274,15 @@ int gqa_decode_ex(int dtype, const void* q, const void* k_cache, const void* v_c
                   const float* alibi_slopes, int num_splits, void* workspace,
                   size_t workspace_bytes, void* stream) {
   DecodePlan plan;
-  if (!plan_decode(B, Hq, Hkv, d > 0 ? d : 1, max_len, num_splits, &plan))
-    return GQA_ERR_INVALID_ARG;
-  if (!q || !k_cache || !v_cache || !o) return GQA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
-    return GQA_ERR_INVALID_ARG;
-  if ((lse && ((uintptr_t)lse & 3u)) || (cache_lens && ((uintptr_t)cache_lens & 3u)) ||
-      (alibi_slopes && ((uintptr_t)alibi_slopes & 3u)) ||
-      (block_table && ((uintptr_t)block_table & 3u)))
-    return GQA_ERR_INVALID_ARG;
-  if (!isfinite(softmax_scale) || window < 0) return GQA_ERR_INVALID_ARG;
-  if (block_table) {
-    // Paged cache: tiles of 32 keys must not straddle pages, and the table covers max_len.
-    if (page_size <= 0 || page_size % kDecodeTile != 0 || max_blocks <= 0 || num_pages <= 0 ||
-        (long long)page_size * max_blocks != max_len)
-      return GQA_ERR_INVALID_ARG;
-  }
-  if (dtype != GQA_DTYPE_BF16) return GQA_ERR_UNSUPPORTED;
-  if (!supported_decode_d(d)) return GQA_ERR_UNSUPPORTED;
+  const int st = check_decode(dtype, q, k_cache, v_cache, cache_lens, block_table, page_size,
+                              max_blocks, num_pages, o, lse, B, Hq, Hkv, d, max_len,
+                              softmax_scale, window, alibi_slopes, num_splits, &plan);
+  if (st != GQA_OK) return st;
   if (!workspace || workspace_bytes < plan.ws_bytes || !aligned16(workspace))
     return GQA_ERR_WORKSPACE;
-
-  gqa::DecodeParams p;
-  p.q = q; p.kc = k_cache; p.vc = v_cache; p.lens = cache_lens; p.o = o; p.lse = lse;
-  p.ws_o = static_cast<float*>(workspace);
-  p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_lse_offset);
-  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.g = Hq / Hkv; p.d = d; p.max_len = max_len;
-  p.nqb = plan.nqb; p.n_units = plan.n_units; p.n_wg = plan.n_wg;
-  // A zero scale (uniform weights) still gets a positive exponent factor, tiny enough
-  // that every valid weight rounds to exp2(0) = 1 while masked scores (-inf) give 0.
-  p.scale_log2 = fmaxf(fabsf(softmax_scale) * kLog2e, kMinScaleLog2);
-  // The LSE converts the kernels' running max (raw-score units) with the scale that factor
-  // stands for, not |softmax_scale|: with a zero scale and ALiBi the max holds a bias of
-  // slope / scale_log2 per key and must still come out as slope * distance.
-  p.scale_abs = p.scale_log2 / kLog2e;
-  p.negate_q = softmax_scale < 0.f ? 1 : 0;
-  p.window = window < max_len ? window : 0;  // a window of max_len or more keys hides nothing
-  p.alibi = alibi_slopes;
-  p.block_table = block_table;
-  p.page_size = block_table ? page_size : 0;
-  p.max_blocks = block_table ? max_blocks : 0;
-  p.num_pages = block_table ? num_pages : 0;
-  // With no length array every unit has the same tile count; one share per unit then
-  // maps each workgroup onto exactly one whole unit and no merge pass is needed.
-  const bool need_combine = !(cache_lens == nullptr && plan.n_wg == plan.n_units);
-  hipError_t e = gqa::launch_decode_bf16(p, need_combine, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+  return launch_decode(q, k_cache, v_cache, cache_lens, block_table, page_size, max_blocks,
+                       num_pages, o, lse, B, Hq, Hkv, d, max_len, softmax_scale, window,
+                       alibi_slopes, plan, workspace, stream);
 }
 
 int gqa_decode(int dtype, const void* q, const void* k_cache, const void* v_cache,

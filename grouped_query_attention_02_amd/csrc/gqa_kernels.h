@@ -66,6 +66,22 @@ struct MeanPoolParams {
   int64_t per_head;   // elements per head, a multiple of 8
 };
 
+// Per-device launch facts, found on the first launch on each device and kept until the
+// process ends (the only state the library keeps between calls).
+constexpr int kMaxDevices = 64;
+
+// The current device and its compute-unit count (queried once per device).
+hipError_t current_device(int* dev_out, int* cus_out);
+
+// One kernel's per-device set-up: the dynamic-LDS attribute is set and the number of its
+// workgroups a CU holds at once is found on the first launch on each device. A zero entry
+// means "not set up yet"; keep one zero-initialised object with static storage per kernel.
+struct KernelSetup {
+  int per_cu[kMaxDevices];
+};
+hipError_t setup_kernel(KernelSetup& s, const void* kern, int threads, size_t lds, int dev,
+                        int* per_cu_out);
+
 hipError_t launch_prefill_bf16(const PrefillParams& p, int causal, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillParams& p, int causal, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeParams& p, bool need_combine, hipStream_t stream);

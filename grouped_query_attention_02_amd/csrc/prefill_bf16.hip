@@ -126,7 +126,7 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int D, bool CAUSAL, bool WINDOW, bool ALIBI>
+template <int D, bool CAUSAL, bool WINDOW, bool ALIBI, bool EXACT_SUM>
 __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) void prefill_bf16_kernel(
     PrefillParams p) {
   using Lay = PfLayout<D>;
@@ -495,6 +495,7 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
     // otherwise key 0 is visible to every row and the first tile always sets it.
     constexpr bool kLateStart = WINDOW || kNearFirst;
     float m_run = kLateStart ? -INFINITY : 0.f, l_run = 0.f;
+    float lx_run = 0.f;  // EXACT_SUM: running sum of the fp32 weights (for the LSE)
 
     // Key j = t0 + 32kb + 8(i/4) + 4hh + (i%4) is kept iff lo <= j < lim: the signs of
     // j - lim and j - lo select between the score and the masked bit pattern (no compare
@@ -560,8 +561,12 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
       return mx;
     };
     // Weights exp2(c sgn s - c m) rounded to bf16 as the PV operand; returns this lane's sum
-    // of the rounded weights (the same values the PV product uses). exp2(-inf) = 0.
-    auto weights = [&](const f32x16 (&sc)[NKB], bf16x8 (&pp)[NKS], int t) {
+    // of the rounded weights (the values the PV product uses, one dot2 per pair: the output
+    // is normalised by exactly the weights it sums, so a row dominated by one key keeps that
+    // key's value whatever the rounding). With EXACT_SUM (the caller asked for the LSE) the
+    // fp32 weights are summed as well, into xsum: that sum carries no bf16 rounding into the
+    // LSE. exp2(-inf) = 0.
+    auto weights = [&](const f32x16 (&sc)[NKB], bf16x8 (&pp)[NKS], int t, float& xsum) {
       const float msc = ((kLateStart && m_run == -INFINITY) ? 0.f : m_run) * c;  // no key yet
       const float dq = ALIBI ? alibi_dq(t) : 0.f;
       const float bc = beta * c;  // the bias slope in exp2 units
@@ -585,6 +590,10 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
           // The dot operand is the converted pair itself: bit-casting it back out of w[i]
           // makes this compiler feed the same register to every dot instruction.
           lsum = __builtin_amdgcn_fdot2_f32_bf16(h, ones2, lsum, false);
+          if constexpr (EXACT_SUM) {
+            xsum += e[0];
+            xsum += e[1];
+          }
         }
         pp[ks] = as_bf16x8(w);
       }
@@ -616,7 +625,8 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
       // while other waves' matrix products are in flight (measured ~2% faster for d = 128,
       // neutral for d = 64).
       __builtin_amdgcn_s_setprio(1);
-      float lsum = weights(sc, pp, t);
+      float xsum = 0.f;
+      float lsum = weights(sc, pp, t, xsum);
       __builtin_amdgcn_s_setprio(0);
       if (wave_any(!(lsum <= kSumCap))) {
         // Recompute the scores from the K tile (still in LDS) rather than keeping them live
@@ -627,14 +637,17 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
         const float m_new = fmaxf(m_run, new_offset(sc, t));
         const float alpha = m_new == m_run ? 1.f : fast_exp2((m_run - m_new) * c);
         l_run *= alpha;
+        if constexpr (EXACT_SUM) lx_run *= alpha;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
           for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
         m_run = m_new;
-        lsum = weights(sc, pp, t);
+        xsum = 0.f;
+        lsum = weights(sc, pp, t, xsum);
       }
       l_run += lsum;
+      if constexpr (EXACT_SUM) lx_run += xsum;
       pv(pp, vslot(u));
     };
 
@@ -648,8 +661,9 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
       block_barrier();              // ... and every wave's; slot u may be overwritten next
     }
 
-    // Epilogue: O = O^T / l, rounded to bf16; LSE = m*|scale| + ln l.
+    // Epilogue: O = O^T / l, rounded to bf16; LSE = m*|scale| + ln l (l of the fp32 weights).
     const float l_tot = pair_sum(l_run);
+    const float lx_tot = EXACT_SUM ? pair_sum(lx_run) : 0.f;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (row_ok) {
       uint16_t* orow = static_cast<uint16_t*>(p.o) + (((size_t)b * S + qi) * Hq + hq) * D;
@@ -663,10 +677,12 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
           w[1] = pack_bf16x2(oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv);
           *reinterpret_cast<u32x2*>(orow + d0) = w;
         }
-      if (p.lse && hh == 0)
-        p.lse[((size_t)b * Hq + hq) * S + qi] =
-            l_tot > 0.f ? m_run * p.scale_abs + logf(l_tot) - slope * (float)(qi - qa)
-                        : -INFINITY;
+      if constexpr (EXACT_SUM) {
+        if (hh == 0)
+          p.lse[((size_t)b * Hq + hq) * S + qi] =
+              l_tot > 0.f ? m_run * p.scale_abs + logf(lx_tot) - slope * (float)(qi - qa)
+                          : -INFINITY;
+      }
     }
   }
   wait_vm<0>();  // drain the copies issued past the last tile
@@ -678,28 +694,20 @@ constexpr size_t prefill_lds_bytes() {
   return PfLayout<D>::LDS_BYTES + 2 * kPrefillLptMaxB * sizeof(int);
 }
 
-// Workgroups of one kernel that a CU holds at once (at least 1).
-template <typename K>
-int resident_per_cu(K kern, int threads, size_t lds) {
-  if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-    return 1;
-  int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, threads, lds) != hipSuccess) return 1;
-  return nb > 0 ? nb : 1;
-}
-
 template <int D, bool CAUSAL, bool WINDOW, bool ALIBI>
 hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
   const size_t lds = prefill_lds_bytes<D>();
-  auto kern = prefill_bf16_kernel<D, CAUSAL, WINDOW, ALIBI>;
-  static const int per_cu = resident_per_cu(kern, PfShape<D>::THREADS, lds);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  // With an LSE output the weight sums are taken in fp32 (a separate instantiation, so the
+  // plain kernel keeps its dot2 sums).
+  auto kern = p.lse ? prefill_bf16_kernel<D, CAUSAL, WINDOW, ALIBI, true>
+                    : prefill_bf16_kernel<D, CAUSAL, WINDOW, ALIBI, false>;
+  static KernelSetup setups[2];  // per device and variant: LDS attribute, workgroups per CU
+  KernelSetup& setup = setups[p.lse ? 1 : 0];
+  int dev = 0, cus = 0, per_cu = 1;
+  hipError_t e = current_device(&dev, &cus);
   if (e != hipSuccess) return e;
-  int dev = 0, cus = 0;
-  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
-  if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+  if ((e = setup_kernel(setup, reinterpret_cast<const void*>(kern), PfShape<D>::THREADS, lds, dev,
+                        &per_cu)) != hipSuccess)
     return e;
   // One resident workgroup per slot: P slots per XCD, each working through its share of
   // the XCD's queue (no more slots than queue positions).

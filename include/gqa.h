@@ -15,8 +15,10 @@
  * Conventions shared by every entry point:
  *   - All array pointers are DEVICE pointers into memory the caller owns. The
  *     library never allocates or frees memory and keeps no pointer after a call
- *     returns. It keeps no state between calls except a per-device cache of
- *     the compute-unit count.
+ *     returns. The only state it keeps between calls is set up once per device,
+ *     on the first call on that device: the compute-unit count, and for each
+ *     kernel its dynamic-LDS attribute and how many of its workgroups a compute
+ *     unit holds.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
  *     and the call returns right after the enqueue. No call synchronises the
  *     host or reads device memory from the host.
@@ -117,15 +119,23 @@ int gqa_prefill_ex(int dtype, const void *q, const void *k, const void *v, void 
 
 /*
  * gqa_decode_workspace_bytes - device workspace gqa_decode needs for these
- * arguments (split partials: normalised fp32 outputs and their log-sum-exp).
- * Returns 0 for invalid arguments.
+ * arguments. The decode splits each cache's keys into pieces (the pages'
+ * `num_splits` knob, gitcode page, "阶段二：高级优化参数"); a piece that does
+ * not cover a whole sequence leaves a partial result, a normalised fp32 output
+ * row per query head plus its log-sum-exp, for the merge. The workspace holds
+ * (split workgroups + units) x 32 such rows, units = B x Hkv x ceil(g / 32).
+ * Host arithmetic only (no HIP call). Returns 0 for invalid arguments.
  */
 size_t gqa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_len, int num_splits);
 
 /*
  * gqa_decode_num_workgroups - number of split workgroups gqa_decode launches
- * for these arguments (the auto rule when num_splits == 0). Returns 0 for
- * invalid arguments.
+ * for these arguments: the `num_splits` knob of the gitcode page ("阶段二：
+ * 高级优化参数") turned into a count of equal shares of the key work. With
+ * num_splits == 0 (automatic) it is max(units, 256), one workgroup per compute
+ * unit of the GPU at least; with n > 0 it is n x units; never more than the
+ * total number of 32-key tiles of max_len-long caches. Host arithmetic only.
+ * Returns 0 for invalid arguments.
  */
 int gqa_decode_num_workgroups(int B, int Hq, int Hkv, int max_len, int num_splits);
 

@@ -27,6 +27,24 @@ F64, F32, BF16 = 0, 1, 2
 _lib = None
 
 
+# A sanitizer build of oracle.c (see build_sanitized) is loaded instead of liboracle.so when
+# this environment variable names it; the process must then have the matching runtime
+# (gcc's libasan) loaded first, e.g. through LD_PRELOAD.
+SANITIZED_ENV = "ORACLE_SANITIZED_LIB"
+
+SANITIZE_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                  "-fno-sanitize-recover=all"]
+
+
+def build_sanitized(path: str) -> str:
+    """Compile oracle.c with AddressSanitizer and UndefinedBehaviorSanitizer into `path`
+    (host code only; the same arithmetic flags as build())."""
+    cmd = ["gcc", *SANITIZE_FLAGS, "-fopenmp", "-fPIC", "-shared", "-std=c11",
+           "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", path, "-lm"]
+    subprocess.run(cmd, check=True)
+    return path
+
+
 def build(force: bool = True) -> str:
     """Compile oracle.c into liboracle.so with gcc (-O2, OpenMP, no fast-math)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
@@ -41,9 +59,12 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build(force=True)
-        lib = ctypes.CDLL(_LIB)
+        path = os.environ.get(SANITIZED_ENV)
+        if not path:
+            path = _LIB
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build(force=True)
+        lib = ctypes.CDLL(path)
         vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
         lib.oracle_prefill_rows.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                             dbl, i32, vp, i64, vp, vp, vp, i32]

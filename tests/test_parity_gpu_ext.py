@@ -2,9 +2,11 @@
 (gqa_prefill_ex / gqa_decode_ex), against the fp64 oracle.
 
 Tolerances are those of test_parity_gpu.py: outputs 1e-5 (fp32) and 2e-2 (bf16);
-LSE 1e-4 (fp32), 4e-3 (bf16 prefill: the weights are summed after rounding to bf16,
-relative error <= 2^-8, so ln(1 + 2^-8) = 3.9e-3) and 1e-3 (bf16 decode), in prefill each
-beyond 2 fp32 ulps of the LSE's own value (its storage precision).
+LSE 1e-4 (fp32) and 1e-3 (bf16: with an LSE output the weights are summed in fp32), in
+prefill each beyond 2 fp32 ulps of the LSE's own value (its storage precision). The one
+exception is the steep-ALiBi stress test, whose q and k are 3x the unit-variance inputs the
+fp32 tolerance is stated for: its logits, and the fp32 rounding error they carry, are 9x
+larger, and so is its fp32 output tolerance.
 """
 import math
 import sys
@@ -19,7 +21,7 @@ import workloads as W
 pytestmark = pytest.mark.gpu
 
 TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-2}
-LSE_TOL = {torch.float32: 1e-4, torch.bfloat16: 4e-3}
+LSE_TOL = {torch.float32: 1e-4, torch.bfloat16: 1e-3}
 DEC_LSE_TOL = 1e-3
 
 
