@@ -17,7 +17,7 @@ from typing import Optional
 from ._lib import (GQA_DTYPE_BF16, GQA_DTYPE_F32, GQA_OK, GQAError, header_functions, load,
                    status_string)
 
-__all__ = ["prefill", "decode", "decode_workspace_bytes", "decode_num_workgroups",
+__all__ = ["prefill", "decode", "decode_noalloc", "decode_workspace_bytes", "decode_num_workgroups",
            "mean_pool_heads", "version", "status_string", "GQAError", "load", "header_functions"]
 
 
@@ -242,6 +242,67 @@ def decode(q, k_cache, v_cache, cache_lens=None, *, softmax_scale: Optional[floa
     if st != GQA_OK:
         raise GQAError(st, "gqa_decode_ex")
     return (out, lse_out) if return_lse else out
+
+
+DECODE_SCRATCH_BYTES = 32 << 20  # GQA_DECODE_SCRATCH_BYTES of include/gqa.h
+
+
+def decode_noalloc(q, k_cache, v_cache, cache_lens, out, *, lse_out=None,
+                   softmax_scale: Optional[float] = None, num_splits: int = 0, window: int = 0,
+                   alibi_slopes=None, block_table=None, page_size: int = 0):
+    """gqa_decode_noalloc: decode() with the library's static device scratch in place of a
+    workspace. Nothing is allocated: `out` ([B, Hq, d], q's dtype) and, when wanted, `lse_out`
+    ([B, Hq] float32) are the caller's; cache_lens and alibi_slopes must already be device
+    tensors of the right dtype (int32 / float32) when given. Calls that overlap in time on one
+    GPU share its scratch and must not be issued concurrently. Returns out (and lse_out)."""
+    torch = _torch()
+    _check(q, "q", 3)
+    _check(k_cache, "k_cache", 4, q.dtype)
+    _check(v_cache, "v_cache", 4, q.dtype)
+    if k_cache.device != q.device or v_cache.device != q.device:
+        raise ValueError("q, k_cache and v_cache must be on the same device")
+    B, Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or k_cache.shape[3] != d:
+        raise ValueError("k_cache and v_cache must have the same shape, last dim d")
+    table_ptr, max_blocks, num_pages = 0, 0, 0
+    if block_table is None:
+        max_len = k_cache.shape[2]
+        if k_cache.shape[0] != B:
+            raise ValueError("k_cache and v_cache must be [B, Hkv, max_len, d]")
+    else:
+        _check(block_table, "block_table", 2, torch.int32)
+        if block_table.device != q.device or block_table.shape[0] != B \
+                or k_cache.shape[2] != page_size:
+            raise ValueError("paged cache: pools [num_pages, Hkv, page_size, d], "
+                             "block_table [B, max_blocks] on q's device")
+        table_ptr = block_table.data_ptr()
+        max_blocks, num_pages = block_table.shape[1], k_cache.shape[0]
+        max_len = max_blocks * page_size
+    if Hkv <= 0 or Hq % Hkv != 0:
+        raise ValueError(f"num_heads_q ({Hq}) must be divisible by num_heads_kv ({Hkv})")
+    _check_buffer(out, "out", q.shape, q.dtype, q.device)
+    if lse_out is not None:
+        _check_buffer(lse_out, "lse_out", (B, Hq), torch.float32, q.device)
+    lens_ptr = 0
+    if cache_lens is not None:
+        _check_buffer(cache_lens, "cache_lens", (B,), torch.int32, q.device)
+        lens_ptr = cache_lens.data_ptr()
+    slopes_ptr = 0
+    if alibi_slopes is not None:
+        _check_buffer(alibi_slopes, "alibi_slopes", (Hq,), torch.float32, q.device)
+        slopes_ptr = alibi_slopes.data_ptr()
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    st = load().gqa_decode_noalloc(_dtype_code(q), q.data_ptr(), k_cache.data_ptr(),
+                                   v_cache.data_ptr(), lens_ptr or None, table_ptr or None,
+                                   int(page_size) if table_ptr else 0, max_blocks, num_pages,
+                                   out.data_ptr(),
+                                   lse_out.data_ptr() if lse_out is not None else None,
+                                   B, Hq, Hkv, d, max_len, scale, int(window), slopes_ptr or None,
+                                   int(num_splits), _stream_ptr(q.device))
+    if st != GQA_OK:
+        raise GQAError(st, "gqa_decode_noalloc")
+    return (out, lse_out) if lse_out is not None else out
 
 
 def mean_pool_heads(w, num_groups: int, *, out=None):

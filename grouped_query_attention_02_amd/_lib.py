@@ -70,6 +70,9 @@ def load():
     lib.gqa_decode_ex.argtypes = [i32, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, i32, i32, i32,
                                   i32, i32, f32, i32, vp, i32, vp, sz, vp]
     lib.gqa_decode_ex.restype = i32
+    lib.gqa_decode_noalloc.argtypes = [i32, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, i32, i32,
+                                       i32, i32, i32, f32, i32, vp, i32, vp]
+    lib.gqa_decode_noalloc.restype = i32
     lib.gqa_mean_pool_heads.argtypes = [i32, vp, i32, i32, ctypes.c_int64, vp, vp]
     lib.gqa_mean_pool_heads.restype = i32
     _lib = lib

@@ -113,6 +113,35 @@ hipError_t setup_kernel(KernelSetup& s, const void* kern, int threads, size_t ld
 
 namespace {
 
+// Device scratch of gqa_decode_noalloc: the split partials of one call, in place of a
+// caller's workspace. Each device the library runs on holds its own copy of this array
+// until the process ends. In host code the name is only a stand-in: its device address is
+// looked up once per device (scratch_address) and only that address is ever passed on.
+static __device__ __align__(256) uint8_t scratch[GQA_DECODE_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device, looked up on the first call on each
+// device and cached.
+hipError_t scratch_address(void** out) {
+  static void* cache[gqa::kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool cached = dev >= 0 && dev < gqa::kMaxDevices;
+  if (cached) {
+    void* ptr = __atomic_load_n(&cache[dev], __ATOMIC_ACQUIRE);
+    if (ptr) {
+      *out = ptr;
+      return hipSuccess;
+    }
+  }
+  void* ptr = nullptr;
+  if ((e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+  if (!ptr) return hipErrorInvalidSymbol;
+  if (cached) __atomic_store_n(&cache[dev], ptr, __ATOMIC_RELEASE);
+  *out = ptr;
+  return hipSuccess;
+}
+
 // Every argument check of a decode call except the workspace's (host only, no HIP call).
 int check_decode(int dtype, const void* q, const void* k_cache, const void* v_cache,
                  const int32_t* cache_lens, const int32_t* block_table, int page_size,
@@ -185,7 +214,9 @@ const char* gqa_status_string(int status) {
     case GQA_OK: return "ok";
     case GQA_ERR_INVALID_ARG: return "invalid argument";
     case GQA_ERR_UNSUPPORTED: return "unsupported head size or dtype";
-    case GQA_ERR_WORKSPACE: return "decode workspace missing or too small";
+    case GQA_ERR_WORKSPACE:
+      return "decode workspace missing or too small (gqa_decode_noalloc: the call needs more "
+             "than the library's static scratch of GQA_DECODE_SCRATCH_BYTES)";
     case GQA_ERR_HIP: return "HIP runtime error";
     default: return "unknown status";
   }
@@ -283,6 +314,24 @@ int gqa_decode_ex(int dtype, const void* q, const void* k_cache, const void* v_c
   return launch_decode(q, k_cache, v_cache, cache_lens, block_table, page_size, max_blocks,
                        num_pages, o, lse, B, Hq, Hkv, d, max_len, softmax_scale, window,
                        alibi_slopes, plan, workspace, stream);
+}
+
+int gqa_decode_noalloc(int dtype, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* cache_lens, const int32_t* block_table, int page_size,
+                       int max_blocks, int num_pages, void* o, float* lse, int B, int Hq,
+                       int Hkv, int d, int max_len, float softmax_scale, int window,
+                       const float* alibi_slopes, int num_splits, void* stream) {
+  DecodePlan plan;
+  const int st = check_decode(dtype, q, k_cache, v_cache, cache_lens, block_table, page_size,
+                              max_blocks, num_pages, o, lse, B, Hq, Hkv, d, max_len,
+                              softmax_scale, window, alibi_slopes, num_splits, &plan);
+  if (st != GQA_OK) return st;
+  if (plan.ws_bytes > (size_t)GQA_DECODE_SCRATCH_BYTES) return GQA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess) return GQA_ERR_HIP;
+  return launch_decode(q, k_cache, v_cache, cache_lens, block_table, page_size, max_blocks,
+                       num_pages, o, lse, B, Hq, Hkv, d, max_len, softmax_scale, window,
+                       alibi_slopes, plan, ws, stream);
 }
 
 int gqa_decode(int dtype, const void* q, const void* k_cache, const void* v_cache,

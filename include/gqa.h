@@ -211,6 +211,32 @@ int gqa_decode_ex(int dtype, const void *q, const void *k_cache, const void *v_c
                   const float *alibi_slopes, int num_splits, void *workspace,
                   size_t workspace_bytes, void *stream);
 
+/* Size of the device scratch gqa_decode_noalloc uses instead of a workspace (32 MiB). */
+#define GQA_DECODE_SCRATCH_BYTES (32u << 20)
+
+/*
+ * gqa_decode_noalloc - gqa_decode_ex without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. The split partials go to a
+ * scratch array of GQA_DECODE_SCRATCH_BYTES that the library holds in device
+ * memory (one per GPU it runs on, kept until the process ends); the call itself
+ * allocates nothing. The first call on a device looks the array's address up
+ * once (a HIP query, no allocation).
+ *
+ * Every argument and result is as for gqa_decode_ex. Additionally returns
+ * GQA_ERR_WORKSPACE when the call needs more than GQA_DECODE_SCRATCH_BYTES,
+ * i.e. when gqa_decode_workspace_bytes(B, Hq, Hkv, d, max_len, num_splits)
+ * exceeds it (nothing is launched). The scratch keeps the last call's contents;
+ * no call relies on what it holds on entry. All calls on one GPU share that
+ * GPU's scratch, so calls that overlap in time on one GPU (different streams or
+ * threads) race and must be serialised by the caller.
+ */
+int gqa_decode_noalloc(int dtype, const void *q, const void *k_cache, const void *v_cache,
+                       const int32_t *cache_lens, const int32_t *block_table, int page_size,
+                       int max_blocks, int num_pages, void *o, float *lse, int B, int Hq,
+                       int Hkv, int d, int max_len, float softmax_scale, int window,
+                       const float *alibi_slopes, int num_splits, void *stream);
+
 /*
  * gqa_mean_pool_heads - convert per-head K or V projection weights of a
  * multi-head checkpoint to G groups: each group's projection becomes the mean

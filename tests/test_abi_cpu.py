@@ -176,3 +176,28 @@ def test_mean_pool_rejects(lib, kw, code):
     a.update(kw)
     assert lib.gqa_mean_pool_heads(a["dtype"], a["w"], a["H"], a["G"], a["per_head"], a["out"],
                                    None) == code
+
+
+def test_decode_noalloc_rejects_on_host(lib):
+    """gqa_decode_noalloc checks every argument like gqa_decode_ex and refuses calls that need
+    more than its static scratch, all before any HIP call (fake pointers are never used)."""
+    def call(**kw):
+        a = dict(dtype=BF16, q=P, k=P, v=P, lens=None, table=None, page=0, mb=0, np_=0, o=P,
+                 lse=None, B=2, Hq=8, Hkv=1, d=128, L=64, scale=0.1, window=0, alibi=None,
+                 splits=0)
+        a.update(kw)
+        return lib.gqa_decode_noalloc(a["dtype"], a["q"], a["k"], a["v"], a["lens"], a["table"],
+                                      a["page"], a["mb"], a["np_"], a["o"], a["lse"], a["B"],
+                                      a["Hq"], a["Hkv"], a["d"], a["L"], a["scale"], a["window"],
+                                      a["alibi"], a["splits"], None)
+    assert call(Hq=6, Hkv=4) == INV
+    assert call(q=None) == INV
+    assert call(k=P + 2) == INV
+    assert call(scale=math.nan) == INV
+    assert call(window=-1) == INV
+    assert call(table=P, page=48, mb=2, np_=4, L=96) == INV       # page not a multiple of 32
+    assert call(d=96) == UNS
+    assert call(dtype=F32) == UNS
+    # 4096 sequences x 8 K/V heads of 8192 keys need far more than the 32 MiB scratch
+    assert call(B=4096, Hq=64, Hkv=8, L=8192) == WS
+    assert gqa.decode_workspace_bytes(4096, 64, 8, 128, 8192) > gqa.DECODE_SCRATCH_BYTES
