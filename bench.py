@@ -478,8 +478,9 @@ def _extended_rows(reps, dev, flush, cases):
 
 def _extra_seeds(dev, flush, reps, n_seeds=2):
     """Each bf16 workload on `n_seeds` further seeds (inputs drawn on the GPU with the same
-    recipe): call time (median of `reps`, flushed) and the max error against the oracle on
-    sampled rows / (b, h) pairs, for the spread of both over inputs."""
+    recipe): call time (median of `reps`, flushed, after half a second of calls to bring the
+    clocks back up) and the max error against the oracle on sampled rows / (b, h) pairs, for
+    the spread of both over inputs."""
     import numpy as np
     import torch
     import workloads as W
@@ -495,6 +496,10 @@ def _extra_seeds(dev, flush, reps, n_seeds=2):
             host = (W.make_prefill if w.kind == "prefill" else W.make_decode)(
                 w, seed, device="cuda")
             c = Case(w, dev, 1, seed=seed, host=host, gen_device="cuda")
+            # the clocks drop while the host works between these runs: settle them first
+            t_end = time.perf_counter() + 0.5
+            while time.perf_counter() < t_end:
+                time_calls(c.run, 4, flush)
             ms = time_calls(c.run, reps, flush)
             torch.cuda.synchronize()
             rng = np.random.default_rng(seed)

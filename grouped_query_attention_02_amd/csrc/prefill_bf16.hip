@@ -17,10 +17,11 @@
 //   O^T += V^T P^T       (A = V^T read from row-major LDS with the transposing
 //                        ds_read_b64_tr_b16, B = P taken straight from the score
 //                        accumulators)
-// on v_mfma_f32_32x32x16_bf16. The kernel is kept small (at most 128 VGPRs for d <= 64)
-// so that several waves share each SIMD and the hardware overlaps one wave's matrix
-// products with another wave's softmax. K/V tiles stream from HBM/L2 straight into a
-// 4-slot LDS ring, three tiles ahead of their use. The exponent offset is a row
+// on v_mfma_f32_32x32x16_bf16. The kernel is kept small (at most 128 VGPRs for d <= 64,
+// 168 for d = 128) so that several waves share each SIMD (four, or three for d = 128) and
+// the hardware overlaps one wave's matrix products with another wave's softmax. K/V tiles
+// stream from HBM/L2 straight into an LDS ring (4 slots, 3 for d = 128), RING - 1 tiles
+// ahead of their use. The exponent offset is a row
 // max that is raised only when a tile's weights would exceed 2^32, so the O rescale is
 // rare; every term of a row always shares one offset, so the normalised result is
 // unchanged. The result equals textbook softmax(scale Q K^T) V
@@ -47,13 +48,18 @@ struct PfShape {
   // Keys per K/V tile: 64 while the registers allow four waves per SIMD, 32 for d = 128.
   static constexpr int BN = D == 128 ? 32 : 64;
   static constexpr int WAVES = D == 128 ? 4 : 8;
-  static constexpr int WG_PER_CU = 2;
+  // d = 128: three 4-wave workgroups per CU, so three waves share each SIMD (at most 168
+  // VGPRs each) and hide each other's LDS and matrix-core latencies (5 % faster than two
+  // workgroups on the causal Llama-shaped prefill). d <= 64: two 8-wave workgroups (four
+  // waves per SIMD at 128 VGPRs).
+  static constexpr int WG_PER_CU = D == 128 ? 3 : 2;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int ROWS = 32 * WAVES;
   static constexpr int WAVES_PER_SIMD = WG_PER_CU * WAVES / 4;  // register budget 512 / this
   // LDS slots per K and per V ring, and tiles in flight ahead of the one being read.
-  // (The 64 KB ring lets two workgroups share a CU; a 3-slot ring measured slower.)
-  static constexpr int RING = 4;
+  // d <= 64: the 64 KB ring lets two workgroups share a CU (a 3-slot ring measured slower);
+  // d = 128: 3-slot rings (48 KB) let three share it.
+  static constexpr int RING = D == 128 ? 3 : 4;
   static constexpr int AHEAD = RING - 1;
   // Persistent launch: one resident workgroup per slot works through a share of its XCD's
   // queue. Used for d = 128 (one wave per SIMD per workgroup), where the two workgroups
@@ -135,7 +141,9 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
   constexpr int ROWS = Shp::ROWS;
   constexpr int PF_BN = Lay::BN;
   constexpr int NKB = Lay::NKB, NKS = Lay::NKS;
-  constexpr bool kBatchReads = D == 128;
+  // (Reading all of a tile's K or V^T fragments before its products, measured ~3 % faster
+  // with two waves per SIMD, does not fit the 168-register budget of three.)
+  constexpr bool kBatchReads = false;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
   // LDS: K slots 0..RING-1, then V slots 0..RING-1 (byte offsets).
@@ -420,9 +428,9 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
     const float sbeta = sgn * beta;
     auto alibi_off = [](int kb, int i) { return (float)(32 * kb + 8 * (i >> 2) + (i & 3)); };
 
-    // S^T = K Q^T. For d = 128 all K fragments of the tile are read from LDS first and the
-    // products then run back to back (measured faster); for d <= 64 each read feeds its
-    // product directly, which keeps the register budget of four waves per SIMD.
+    // S^T = K Q^T. Each fragment read feeds its product directly, which keeps the register
+    // budgets (four waves per SIMD at d <= 64, three at d = 128); kBatchReads reads all of
+    // a tile's fragments first.
     auto qk = [&](f32x16 (&sc)[NKB], int slot_off) {
       auto kfrag = [&](int ks, int kb) {
         return *reinterpret_cast<const u32x4*>(smem + slot_off + kb * 32 * Lay::ROWB + k_lane +
@@ -460,7 +468,7 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
       }
     };
     // O^T += V^T P^T, 16 keys per MFMA; B slot i <-> key 16ks + 8(i/4) + 4hh + (i%4). The
-    // V^T fragments come from transposing reads (batched first for d = 128, as for K).
+    // V^T fragments come from transposing reads.
     auto pv = [&](const bf16x8 (&pp)[NKS], int slot_off) {
       auto vfrag = [&](int ks, int db) {
         const int off = slot_off + ks * 16 * Lay::ROWB + v_lane + 16 * ((4 * db + tr_q) ^ v_swz);
