@@ -111,9 +111,12 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t num_bytes)
 // 1 KB per wave, straight into LDS at m0 + 16 * lane with no VGPR staging. Out-of-range
 // chunks arrive as zeros. Issued as inline asm so the compiler does not turn every later
 // LDS read into a wait for all outstanding copies; the kernel waits on the
-// vector-memory counter itself before each barrier.
+// vector-memory counter itself before each barrier. The compiler inserts no hazard waits
+// around inline asm, so the asm carries them: on GFX9 a buffer instruction must issue at
+// least 5 wait states after a vector instruction wrote one of its descriptor's SGPRs
+// (make_rsrc's readfirstlane calls) and an LDS copy at least 1 after a scalar write of M0.
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc),
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc),
                "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
                : "memory");
 }
