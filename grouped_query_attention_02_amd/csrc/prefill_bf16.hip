@@ -18,10 +18,10 @@
 //                        ds_read_b64_tr_b16, B = P taken straight from the score
 //                        accumulators)
 // on v_mfma_f32_32x32x16_bf16. The kernel is kept small (at most 128 VGPRs for d <= 64,
-// 168 for d = 128) so that several waves share each SIMD (four, or three for d = 128) and
-// the hardware overlaps one wave's matrix products with another wave's softmax. K/V tiles
-// stream from HBM/L2 straight into an LDS ring (4 slots, 3 for d = 128), RING - 1 tiles
-// ahead of their use. The exponent offset is a row
+// 168 for d = 128 without ALiBi) so that several waves share each SIMD (four, or three for
+// d = 128; two for d = 128 with ALiBi) and the hardware overlaps one wave's matrix
+// products with another wave's softmax. K/V tiles stream from HBM/L2 straight into an LDS
+// ring (4 slots, 3 with three workgroups per CU), RING - 1 tiles ahead of their use. The exponent offset is a row
 // max that is raised only when a tile's weights would exceed 2^32, so the O rescale is
 // rare; every term of a row always shares one offset, so the normalised result is
 // unchanged. The result equals textbook softmax(scale Q K^T) V
@@ -42,24 +42,30 @@ namespace {
 
 constexpr float kSumCap = 4294967296.0f;  // 2^32: a tile's weights stay at most this large
 
-// Waves per workgroup and workgroups per CU for head size D.
-template <int D>
+// Waves per workgroup and workgroups per CU for head size D (and the ALiBi flag, whose
+// extra registers change the d = 128 choice).
+template <int D, bool ALIBI = false>
 struct PfShape {
   // Keys per K/V tile: 64 while the registers allow four waves per SIMD, 32 for d = 128.
   static constexpr int BN = D == 128 ? 32 : 64;
   static constexpr int WAVES = D == 128 ? 4 : 8;
   // d = 128: three 4-wave workgroups per CU, so three waves share each SIMD (at most 168
   // VGPRs each) and hide each other's LDS and matrix-core latencies (5 % faster than two
-  // workgroups on the causal Llama-shaped prefill). d <= 64: two 8-wave workgroups (four
-  // waves per SIMD at 128 VGPRs).
-  static constexpr int WG_PER_CU = D == 128 ? 3 : 2;
+  // workgroups on the causal Llama-shaped prefill). The ALiBi kernels spill 16-23
+  // registers at that budget, so they keep two workgroups per CU (256 VGPRs, no spills).
+  // d <= 64: two 8-wave workgroups (four waves per SIMD at 128 VGPRs).
+  static constexpr bool THREE = D == 128 && !ALIBI;
+  static constexpr int WG_PER_CU = THREE ? 3 : 2;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int ROWS = 32 * WAVES;
   static constexpr int WAVES_PER_SIMD = WG_PER_CU * WAVES / 4;  // register budget 512 / this
   // LDS slots per K and per V ring, and tiles in flight ahead of the one being read.
-  // d <= 64: the 64 KB ring lets two workgroups share a CU (a 3-slot ring measured slower);
-  // d = 128: 3-slot rings (48 KB) let three share it.
-  static constexpr int RING = D == 128 ? 3 : 4;
+  // With two workgroups per CU the 64 KB ring (4 slots) lets both share it (a 3-slot ring
+  // measured slower); with three (d = 128), 3-slot rings (48 KB each).
+  static constexpr int RING = THREE ? 3 : 4;
+  // Read all of a tile's K or V^T fragments before its products: ~3 % faster at d = 128
+  // with two waves per SIMD, but beyond the 168-register budget of three.
+  static constexpr bool BATCH_READS = D == 128 && !THREE;
   static constexpr int AHEAD = RING - 1;
   // Persistent launch: one resident workgroup per slot works through a share of its XCD's
   // queue. Used for d = 128 (one wave per SIMD per workgroup), where the two workgroups
@@ -74,16 +80,16 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-template <int D>
+template <int D, bool ALIBI>
 struct PfLayout {
-  static constexpr int BN = PfShape<D>::BN;
+  static constexpr int BN = PfShape<D, ALIBI>::BN;
   static constexpr int NKB = BN / 32;            // 32-key score blocks per tile
   static constexpr int NKS = BN / 16;            // 16-key MFMA steps per tile
   static constexpr int CPR = D / 8;              // 16-byte chunks per row
   static constexpr int ROWB = D * 2;             // bytes per K or V row
   static constexpr int TILE_B = BN * ROWB;       // bytes per K or V tile
   static constexpr int NWI = BN * CPR / 64;      // 1 KB DMA wave-instructions per tile
-  static constexpr int LDS_BYTES = 2 * PfShape<D>::RING * TILE_B;
+  static constexpr int LDS_BYTES = 2 * PfShape<D, ALIBI>::RING * TILE_B;
   // Tiles are stored unpadded (DMA writes 1 KB contiguous per wave instruction); the
   // 16-byte chunk q of row r sits at chunk position q ^ f(r). fk makes the K fragment
   // reads (16 rows x one chunk per pass) hit 16 different bank groups; fv does the same
@@ -136,17 +142,16 @@ __device__ __forceinline__ void block_barrier() {
 }
 
 template <int D, bool CAUSAL, bool WINDOW, bool ALIBI, bool EXACT_SUM>
-__global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) void prefill_bf16_kernel(
-    PrefillParams p) {
-  using Lay = PfLayout<D>;
-  using Shp = PfShape<D>;
+__global__ __launch_bounds__((PfShape<D, ALIBI>::THREADS),
+                             (PfShape<D, ALIBI>::WAVES_PER_SIMD)) void
+prefill_bf16_kernel(PrefillParams p) {
+  using Lay = PfLayout<D, ALIBI>;
+  using Shp = PfShape<D, ALIBI>;
   constexpr int WAVES = Shp::WAVES;
   constexpr int ROWS = Shp::ROWS;
   constexpr int PF_BN = Lay::BN;
   constexpr int NKB = Lay::NKB, NKS = Lay::NKS;
-  // (Reading all of a tile's K or V^T fragments before its products, measured ~3 % faster
-  // with two waves per SIMD, does not fit the 168-register budget of three.)
-  constexpr bool kBatchReads = false;
+  constexpr bool kBatchReads = Shp::BATCH_READS;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
   // LDS: K slots 0..RING-1, then V slots 0..RING-1 (byte offsets).
@@ -700,14 +705,15 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::WAVES_PER_SIMD) vo
 }
 
 // Dynamic LDS of the kernel: the K/V ring, then the length-order tables.
-template <int D>
+template <int D, bool ALIBI>
 constexpr size_t prefill_lds_bytes() {
-  return PfLayout<D>::LDS_BYTES + 2 * kPrefillLptMaxB * sizeof(int);
+  return PfLayout<D, ALIBI>::LDS_BYTES + 2 * kPrefillLptMaxB * sizeof(int);
 }
 
 template <int D, bool CAUSAL, bool WINDOW, bool ALIBI>
 hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
-  const size_t lds = prefill_lds_bytes<D>();
+  using Shp = PfShape<D, ALIBI>;
+  const size_t lds = prefill_lds_bytes<D, ALIBI>();
   // With an LSE output the weight sums are taken in fp32 (a separate instantiation, so the
   // plain kernel keeps its dot2 sums).
   auto kern = p.lse ? prefill_bf16_kernel<D, CAUSAL, WINDOW, ALIBI, true>
@@ -717,14 +723,14 @@ hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
   int dev = 0, cus = 0, per_cu = 1;
   hipError_t e = current_device(&dev, &cus);
   if (e != hipSuccess) return e;
-  if ((e = setup_kernel(setup, reinterpret_cast<const void*>(kern), PfShape<D>::THREADS, lds, dev,
+  if ((e = setup_kernel(setup, reinterpret_cast<const void*>(kern), Shp::THREADS, lds, dev,
                         &per_cu)) != hipSuccess)
     return e;
   // One resident workgroup per slot: P slots per XCD, each working through its share of
   // the XCD's queue (no more slots than queue positions).
-  const int slots = PfShape<D>::PERSISTENT ? per_cu * (cus / 8 > 0 ? cus / 8 : 1) : p.per_xcd;
+  const int slots = Shp::PERSISTENT ? per_cu * (cus / 8 > 0 ? cus / 8 : 1) : p.per_xcd;
   const int P = p.per_xcd < slots ? p.per_xcd : slots;
-  hipLaunchKernelGGL(kern, dim3(8 * (P > 0 ? P : 1)), dim3(PfShape<D>::THREADS), lds, stream, p);
+  hipLaunchKernelGGL(kern, dim3(8 * (P > 0 ? P : 1)), dim3(Shp::THREADS), lds, stream, p);
   return hipGetLastError();
 }
 
@@ -743,6 +749,9 @@ hipError_t launch_d(const PrefillParams& p, int causal, hipStream_t stream) {
 }
 
 }  // namespace
+
+static_assert(PfShape<128, true>::ROWS == PfShape<128, false>::ROWS,
+              "the host plans one row count per head size");
 
 int prefill_rows_per_wg_bf16(int d) {
   return d == 128 ? PfShape<128>::ROWS : (d == 64 ? PfShape<64>::ROWS : PfShape<32>::ROWS);
