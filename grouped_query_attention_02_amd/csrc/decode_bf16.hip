@@ -127,6 +127,59 @@ __device__ void find_seq(const int32_t* lens, int B, int cap, int window, long l
   *start_out = scratch[DC_WAVES + 1];
 }
 
+// The workgroup's share [t_begin, t_end) of the concatenated unit tiles (T of them, W =
+// min(T, n_wg) equal shares) and the sequence b it starts in, with bstart that sequence's
+// first tile. With at most one length per thread this is one pass over the lengths (a
+// workgroup-wide scan: the total, then the sequence holding t_begin); longer length
+// arrays take the two-pass path. False when the workgroup has no share (uniform).
+__device__ bool find_share(const DecodeParams& p, int cap, long long HU, int w,
+                           long long* t_begin, long long* t_end, int* b_out,
+                           long long* bstart_out, long long* scratch) {
+  long long T;
+  if (p.B <= DC_THREADS) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const long long tb = tid < p.B ? HU * tiles_of(clamp_len(p.lens, tid, cap), p.window) : 0;
+    long long x = tb;  // inclusive scan within the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const long long y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) scratch[wave] = x;
+    __syncthreads();
+    long long wave_off = 0;
+    T = 0;
+#pragma unroll
+    for (int i = 0; i < DC_WAVES; ++i) {
+      const long long v = scratch[i];
+      wave_off += i < wave ? v : 0;
+      T += v;
+    }
+    const long long W = T < p.n_wg ? T : p.n_wg;
+    if (w >= W) return false;
+    *t_begin = (long long)w * T / W;
+    *t_end = (long long)(w + 1) * T / W;
+    const long long incl = wave_off + x, excl = incl - tb;
+    if (tid < p.B && excl <= *t_begin && *t_begin < incl) {
+      scratch[DC_WAVES] = tid;
+      scratch[DC_WAVES + 1] = excl;
+    }
+    __syncthreads();
+    *b_out = (int)scratch[DC_WAVES];
+    *bstart_out = scratch[DC_WAVES + 1];
+    return true;
+  }
+  long long unused;
+  tile_prefix<DC_THREADS>(p.lens, p.B, cap, p.window, 0, &T, &unused, scratch);
+  T *= HU;
+  const long long W = T < p.n_wg ? T : p.n_wg;
+  if (w >= W) return false;
+  *t_begin = (long long)w * T / W;
+  *t_end = (long long)(w + 1) * T / W;
+  find_seq(p.lens, p.B, cap, p.window, HU, *t_begin, b_out, bstart_out, scratch);
+  return true;
+}
+
 template <int D>
 struct DcLayout {
   static constexpr int OSTR = D + 4;  // floats per query row of a wave's O in LDS
@@ -156,20 +209,12 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_split_kernel(DecodeParam
   const long long HU = (long long)p.Hkv * p.nqb;
   const float c = p.scale_log2;
 
-  long long T, unused;
-  tile_prefix<DC_THREADS>(p.lens, p.B, cap, p.window, 0, &T, &unused, scratch);
-  T *= HU;
   // Never more shares than tiles, so every share is non-empty and the shares
   // overlapping a unit form one run of consecutive workgroups.
-  const long long W = T < p.n_wg ? T : p.n_wg;
-  if (w >= W) return;
-  const long long t_begin = (long long)w * T / W;
-  const long long t_end = (long long)(w + 1) * T / W;
-  if (t_begin >= t_end) return;
-
+  long long t_begin, t_end, bstart;
   int b;
-  long long bstart;
-  find_seq(p.lens, p.B, cap, p.window, HU, t_begin, &b, &bstart, scratch);
+  if (!find_share(p, cap, HU, w, &t_begin, &t_end, &b, &bstart, scratch)) return;
+  if (t_begin >= t_end) return;
 
   const uint32_t flip = p.negate_q ? 0x80008000u : 0u;
   long long t = t_begin;
