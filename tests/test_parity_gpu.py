@@ -118,10 +118,12 @@ def test_prefill_edge_lengths_and_scales(oracle_mod, dtype):
 
 @pytest.mark.parametrize("B,S,Hq,Hkv,d", [(40, 70, 4, 2, 64), (19, 130, 6, 3, 128),
                                            (100, 40, 4, 2, 64), (90, 50, 8, 2, 128),
-                                           (300, 20, 2, 1, 32)])
+                                           (300, 20, 2, 1, 32), (256, 40, 4, 2, 128),
+                                           (257, 40, 4, 1, 128), (257, 45, 4, 2, 64)])
 def test_prefill_many_ragged_sequences(oracle_mod, B, S, Hq, Hkv, d):
     """Many sequences with repeated, zero and over-long lengths: the bf16 kernel orders its
-    work by sequence length (up to 256 sequences) and must still write every output once."""
+    work by sequence length (up to 256 sequences; 257 take the unordered path) and must
+    still write every output once."""
     rng = np.random.default_rng(B + S)
     lens = rng.integers(0, S + 1, size=B)
     lens[: B // 4] = lens[B // 4]          # ties
@@ -307,11 +309,13 @@ def test_decode_sweep(oracle_mod, d, Hq, Hkv):
             assert e <= 2e-2 and le <= BF16_DECODE_LSE_TOL
 
 
-@pytest.mark.parametrize("d", [64, 128])
-def test_decode_many_sequences(oracle_mod, d):
-    """1300 sequences (the split kernel scans lengths 512 at a time, the combine kernel 64 at a
-    time), lengths 0..200 with runs of empty caches: every share still finds its sequence."""
-    B, Hq, Hkv, max_len = 1300, 8, 2, 200
+@pytest.mark.parametrize("d,B", [(64, 1300), (128, 1300), (128, 512), (128, 513)])
+def test_decode_many_sequences(oracle_mod, d, B):
+    """Up to 1300 sequences, lengths 0..200 with runs of empty caches: every share still
+    finds its sequence. The split kernel finds its share in one scan of up to 512 lengths
+    (one per thread) and in two passes of 512 at a time beyond that; the combine kernel
+    scans 64 at a time."""
+    Hq, Hkv, max_len = 8, 2, 200
     _say(f"case decode many sequences B={B} d={d}")
     rng = np.random.default_rng(77 + d)
     lens = rng.integers(0, max_len + 1, size=B)
