@@ -186,6 +186,13 @@ struct DcLayout {
   static constexpr int O_FLOATS = DC_WAVES * 32 * OSTR;
   static constexpr int QSTR = D + 8;  // bf16 per query row of Q in LDS (conflict-free reads)
   static constexpr int Q_BYTES = 32 * QSTR * 2;
+  // Q, the merge area (O, m, l per wave), the share-search scratch, then the clamped
+  // lengths of up to DC_THREADS sequences (kept when the share search read them all).
+  static constexpr size_t SCRATCH_OFF = Q_BYTES + (O_FLOATS + 2 * DC_WAVES * 32) * 4;
+  static constexpr size_t LEN_OFF = SCRATCH_OFF + (DC_WAVES + 4) * sizeof(long long);
+  static constexpr size_t LDS = LEN_OFF + DC_THREADS * sizeof(int);
+  static_assert(LDS <= 160 * 1024, "one workgroup's LDS must fit a CU");
+  static_assert(32 * (D / 8) <= DC_THREADS, "one Q chunk per thread at most");
 };
 
 template <int D, bool ALIBI, bool PAGED>
@@ -193,11 +200,13 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_split_kernel(DecodeParam
   constexpr int DPL = D / 32;  // output columns per lane in the V^T operand
   using Lay = DcLayout<D>;
   extern __shared__ __attribute__((aligned(16))) float dsm[];
+  uint8_t* const dsm8 = reinterpret_cast<uint8_t*>(dsm);
   uint16_t* s_q = reinterpret_cast<uint16_t*>(dsm);                       // [32][QSTR] bf16
   float* s_o = dsm + Lay::Q_BYTES / 4;     // [wave][32][OSTR]
   float* s_m = s_o + Lay::O_FLOATS;        // [wave][32]
   float* s_l = s_m + DC_WAVES * 32;        // [wave][32]
-  long long* scratch = reinterpret_cast<long long*>(s_l + DC_WAVES * 32);  // 8 entries
+  long long* scratch = reinterpret_cast<long long*>(dsm8 + Lay::SCRATCH_OFF);  // 8 + 4 entries
+  int* s_len = reinterpret_cast<int*>(dsm8 + Lay::LEN_OFF);                    // [B] clamped
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -209,152 +218,204 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_split_kernel(DecodeParam
   const long long HU = (long long)p.Hkv * p.nqb;
   const float c = p.scale_log2;
 
+  // With one length per thread the lengths stay in LDS for the segment lookups below.
+  const bool lens_in_lds = p.B <= DC_THREADS;
+  if (lens_in_lds && tid < p.B) s_len[tid] = clamp_len(p.lens, tid, cap);
+
   // Never more shares than tiles, so every share is non-empty and the shares
   // overlapping a unit form one run of consecutive workgroups.
   long long t_begin, t_end, bstart;
   int b;
   if (!find_share(p, cap, HU, w, &t_begin, &t_end, &b, &bstart, scratch)) return;
-  if (t_begin >= t_end) return;
+  if (t_begin >= t_end) return;  // (find_share's barriers also publish s_len)
 
-  const uint32_t flip = p.negate_q ? 0x80008000u : 0u;
-  long long t = t_begin;
-  while (t < t_end && b < p.B) {
-    const int Lb = clamp_len(p.lens, b, cap);
-    const int Tb = tiles_of(Lb, p.window);
-    const int ft = first_tile(Lb, p.window);                   // unit tile tt is key tile ft + tt
-    const int klo = p.window > 0 ? max(0, Lb - p.window) : 0;  // keys j < klo are outside
-    const long long bend = bstart + HU * Tb;
-    if (Tb == 0 || t >= bend) {
-      bstart = bend;
-      ++b;
-      continue;
+  // A segment: the tiles [ta, te) of one unit u = (b, kvh, query block) that fall inside
+  // the share; next_t is the share position after it. All fields are wave-uniform.
+  struct Seg {
+    int b, Lb, Tb, ft, klo, ta, te, kvh, hbase, nh, u;
+    long long next_t;
+  };
+  // The segment holding share position t; b_/bstart_ (the sequence reached so far and its
+  // first position) move forward past sequences that end before t. False at the end of
+  // the share or of the batch.
+  auto find_seg = [&](long long t, int& b_, long long& bstart_, Seg& sg) -> bool {
+    while (t < t_end && b_ < p.B) {
+      const int Lb = lens_in_lds ? s_len[b_] : clamp_len(p.lens, b_, cap);
+      const int Tb = tiles_of(Lb, p.window);
+      const long long bend = bstart_ + HU * Tb;
+      if (Tb == 0 || t >= bend) {
+        bstart_ = bend;
+        ++b_;
+        continue;
+      }
+      const int ui = (int)((t - bstart_) / Tb);
+      const long long ustart = bstart_ + (long long)ui * Tb;
+      const int kvh = ui / p.nqb, qb = ui - kvh * p.nqb;
+      sg.b = b_;
+      sg.Lb = Lb;
+      sg.Tb = Tb;
+      sg.ft = first_tile(Lb, p.window);                   // unit tile tt is key tile ft + tt
+      sg.klo = p.window > 0 ? max(0, Lb - p.window) : 0;  // keys j < klo are outside
+      sg.ta = (int)(t - ustart);
+      sg.te = (int)(min(t_end, ustart + Tb) - ustart);
+      sg.kvh = kvh;
+      sg.hbase = kvh * p.g + qb * 32;
+      sg.nh = min(32, p.g - qb * 32);
+      sg.u = (b_ * p.Hkv + kvh) * p.nqb + qb;
+      sg.next_t = ustart + sg.te;
+      return true;
     }
-    const int ui = (int)((t - bstart) / Tb);
-    const long long ustart = bstart + (long long)ui * Tb;
-    const int ta = (int)(t - ustart);
-    const int te = (int)(min(t_end, ustart + Tb) - ustart);
-    const int kvh = ui / p.nqb, qb = ui - kvh * p.nqb;
-    const int hbase = kvh * p.g + qb * 32;
-    const int nh = min(32, p.g - qb * 32);
-    const int u = (b * p.Hkv + kvh) * p.nqb + qb;
+    return false;
+  };
 
-    const size_t cache_off = PAGED ? 0 : ((size_t)(b * p.Hkv + kvh) * cap) * D;
-    const uint16_t* kb_ = static_cast<const uint16_t*>(p.kc) + cache_off;
-    const uint16_t* vb_ = static_cast<const uint16_t*>(p.vc) + cache_off;
+  // One tile's K rows (A operand: lane reads 16 bytes of row j0 + l32) and V rows (for
+  // 16-key step ks2 and slot i, key j0 + 16ks2 + 8(i/4) + 4hh + (i%4); the lane reads DPL
+  // consecutive values starting at d = DPL * l32). Loads go through a buffer resource that
+  // starts at the tile and ends at row L_b, so rows at or past L_b read as zeros, the lane
+  // offsets are the same for every tile and no load needs a predicate.
+  struct TileRegs {
+    u32x4 kf[D / 16];
+    uint32_t vl[2][8][DPL / 2];
+  };
+  const uint32_t row_b = D * 2;
+  const uint32_t k_lane = l32 * row_b + hh * 16;
+  const uint32_t v_lane = (4 * hh) * row_b + DPL * 2 * l32;
+  // Element offset (from the start of the cache or page pool) of segment tile tt's first
+  // key row and the bytes of its valid rows. A paged cache looks the tile's page up in the
+  // block table (a tile never straddles pages); a page id outside the pool leaves no valid
+  // bytes, so its rows read as zeros.
+  auto tile_src = [&](const Seg& sg, int tt, uint32_t* valid) -> size_t {
+    const int j0 = (sg.ft + tt) * DC_TILE;
+    const int nv = max(min(sg.Lb - j0, DC_TILE), 0);
+    if constexpr (PAGED) {
+      const int page = p.block_table[(size_t)sg.b * p.max_blocks + j0 / p.page_size];
+      const bool ok = page >= 0 && page < p.num_pages;
+      *valid = ok ? (uint32_t)nv * row_b : 0u;
+      return ok ? (((size_t)page * p.Hkv + sg.kvh) * p.page_size + j0 % p.page_size) * D : 0;
+    } else {
+      *valid = (uint32_t)nv * row_b;
+      return (((size_t)sg.b * p.Hkv + sg.kvh) * cap + j0) * D;
+    }
+  };
+  // Every input of the descriptor is wave-uniform; reading each through readfirstlane
+  // tells the compiler so, which keeps every buffer load a single instruction (a
+  // descriptor it cannot prove uniform gets a loop over the distinct values per load).
+  auto rsrc = [&](const void* base, const Seg& sg, int tt) {
+    uint32_t valid;
+    const size_t off = tile_src(sg, tt, &valid);
+    // (readfirstlane returns a signed int: go through uint32_t so that an address whose
+    // low word has bit 31 set is not sign-extended into the high word.)
+    const uint64_t a = reinterpret_cast<uint64_t>(static_cast<const uint16_t*>(base) + off);
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(lo | (hi << 32)), 0,
+                                             __builtin_amdgcn_readfirstlane(valid), 0x00020000);
+  };
+  auto load_k_from = [&](TileRegs& r, __amdgpu_buffer_rsrc_t rk) {
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+      r.kf[ks] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_lane + ks * 32, 0, 0));
+  };
+  auto load_v_from = [&](TileRegs& r, __amdgpu_buffer_rsrc_t rv) {
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t off = v_lane + (16 * ks2 + 8 * (i >> 2) + (i & 3)) * row_b;
+        if constexpr (DPL == 4) {
+          const u32x2 x =
+              __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, off, 0, 0));
+          r.vl[ks2][i][0] = x[0];
+          r.vl[ks2][i][1] = x[1];
+        } else {
+          r.vl[ks2][i][0] = __builtin_amdgcn_raw_buffer_load_b32(rv, off, 0, 0);
+        }
+      }
+  };
+  auto load_k = [&](TileRegs& r, const Seg& sg, int tt) { load_k_from(r, rsrc(p.kc, sg, tt)); };
+  auto load_v = [&](TileRegs& r, const Seg& sg, int tt) { load_v_from(r, rsrc(p.vc, sg, tt)); };
+  // Q of a segment's heads (rows past nh are zeros): thread tid holds 16-byte chunk tid;
+  // it is written to LDS (the B operand of S^T = K Q^T, read back per tile: lane holds
+  // head l32, d = ks*16 + hh*8 .. +7) once the previous segment is done with it.
+  const uint32_t flip = p.negate_q ? 0x80008000u : 0u;
+  const int q_row = tid / (D / 8), q_col = tid - q_row * (D / 8);
+  auto load_q = [&](const Seg& sg) -> u32x4 {
+    u32x4 v = zero_u32x4();
+    if (q_row < 32 && q_row < sg.nh) {
+      v = ldg16(static_cast<const uint16_t*>(p.q) + ((size_t)sg.b * p.Hq + sg.hbase + q_row) * D +
+                q_col * 8);
+      v[0] ^= flip; v[1] ^= flip; v[2] ^= flip; v[3] ^= flip;
+    }
+    return v;
+  };
+  auto store_q = [&](const u32x4& v) {
+    if (q_row < 32) *reinterpret_cast<u32x4*>(s_q + q_row * Lay::QSTR + q_col * 8) = v;
+  };
+
+  Seg cur;
+  if (!find_seg(t_begin, b, bstart, cur)) return;  // uniform
+  TileRegs r0;
+  // The wave's first K/V tile is requested before the Q staging so both round trips
+  // overlap. Later segments' first tiles are requested while the previous segment ends.
+  if (cur.ta + wave < cur.te) {
+    load_k(r0, cur, cur.ta + wave);
+    load_v(r0, cur, cur.ta + wave);
+  }
+  store_q(load_q(cur));
+  __syncthreads();
+
+  for (;;) {
+    // The next segment, if any: only the descriptors of this wave's first tile there stay
+    // live through the tile loop (the segment itself is looked up again at the switch).
+    bool pre_next = false;
+    __amdgpu_buffer_rsrc_t rk_next = __builtin_amdgcn_make_buffer_rsrc(nullptr, 0, 0, 0);
+    __amdgpu_buffer_rsrc_t rv_next = rk_next;
+    {
+      Seg nxt;
+      int bn = b;
+      long long bsn = bstart;
+      if (find_seg(cur.next_t, bn, bsn, nxt) && nxt.ta + wave < nxt.te) {
+        pre_next = true;
+        rk_next = rsrc(p.kc, nxt, nxt.ta + wave);
+        rv_next = rsrc(p.vc, nxt, nxt.ta + wave);
+      }
+    }
 
     f32x16 oacc[DPL];
 #pragma unroll
     for (int i = 0; i < DPL; ++i) oacc[i] = zero16();
     float m_run = -INFINITY, l_run = 0.f;
-
-    // One tile's K rows (A operand: lane reads 16 bytes of row j0 + l32) and V rows (for
-    // 16-key step ks2 and slot i, key j0 + 16ks2 + 8(i/4) + 4hh + (i%4); the lane reads DPL
-    // consecutive values starting at d = DPL * l32). Loads go through a buffer resource that
-    // starts at the tile and ends at row L_b, so rows at or past L_b read as zeros, the lane
-    // offsets are the same for every tile and no load needs a predicate.
-    struct TileRegs {
-      u32x4 kf[D / 16];
-      uint32_t vl[2][8][DPL / 2];
-    };
-    const uint32_t row_b = D * 2;
-    const uint32_t k_lane = l32 * row_b + hh * 16;
-    const uint32_t v_lane = (4 * hh) * row_b + DPL * 2 * l32;
-    // Element offset of unit tile tt's first key row and the bytes of its valid rows. A
-    // paged cache looks the tile's page up in the block table (a tile never straddles
-    // pages); a page id outside the pool leaves no valid bytes, so its rows read as zeros.
-    auto tile_src = [&](int tt, uint32_t* valid) -> size_t {
-      const int j0 = (ft + tt) * DC_TILE;
-      const int nv = max(min(Lb - j0, DC_TILE), 0);
-      if constexpr (PAGED) {
-        const int page = p.block_table[(size_t)b * p.max_blocks + j0 / p.page_size];
-        const bool ok = page >= 0 && page < p.num_pages;
-        *valid = ok ? (uint32_t)nv * row_b : 0u;
-        return ok ? (((size_t)page * p.Hkv + kvh) * p.page_size + j0 % p.page_size) * D : 0;
-      } else {
-        *valid = (uint32_t)nv * row_b;
-        return (size_t)j0 * D;
-      }
-    };
-    // Every input of the descriptor is wave-uniform; reading each through readfirstlane
-    // tells the compiler so, which keeps every buffer load a single instruction (a
-    // descriptor it cannot prove uniform gets a loop over the distinct values per load).
-    auto rsrc = [&](const uint16_t* base, int tt) {
-      uint32_t valid;
-      const size_t off = tile_src(tt, &valid);
-      // (readfirstlane returns a signed int: go through uint32_t so that an address whose
-      // low word has bit 31 set is not sign-extended into the high word.)
-      const uint64_t a = reinterpret_cast<uint64_t>(base + off);
-      const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
-      const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-      return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(lo | (hi << 32)), 0,
-                                               __builtin_amdgcn_readfirstlane(valid),
-                                               0x00020000);
-    };
-    auto load_k = [&](TileRegs& r, int tt) {
-      const __amdgpu_buffer_rsrc_t rk = rsrc(kb_, tt);
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks)
-        r.kf[ks] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_lane + ks * 32, 0, 0));
-    };
-    auto load_v = [&](TileRegs& r, int tt) {
-      const __amdgpu_buffer_rsrc_t rv = rsrc(vb_, tt);
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t off = v_lane + (16 * ks2 + 8 * (i >> 2) + (i & 3)) * row_b;
-          if constexpr (DPL == 4) {
-            const u32x2 x =
-                __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, off, 0, 0));
-            r.vl[ks2][i][0] = x[0];
-            r.vl[ks2][i][1] = x[1];
-          } else {
-            r.vl[ks2][i][0] = __builtin_amdgcn_raw_buffer_load_b32(rv, off, 0, 0);
-          }
-        }
-    };
-    TileRegs r0;
-    // Q of the block's heads -> LDS (rows past nh are zeros); the B operand of S^T = K Q^T
-    // is read back per tile: lane holds head l32, d = ks*16 + hh*8 .. +7. The wave's first
-    // K/V tile is requested before the Q staging so both round trips overlap.
-    if (ta + wave < te) {
-      load_k(r0, ta + wave);
-      load_v(r0, ta + wave);
-    }
-    {
-      const uint16_t* qsrc = static_cast<const uint16_t*>(p.q) + ((size_t)b * p.Hq + hbase) * D;
-      for (int ci = tid; ci < 32 * (D / 8); ci += DC_THREADS) {
-        const int row = ci / (D / 8), col = ci - row * (D / 8);
-        u32x4 v = row < nh ? ldg16(qsrc + (size_t)row * D + col * 8) : zero_u32x4();
-        v[0] ^= flip; v[1] ^= flip; v[2] ^= flip; v[3] ^= flip;
-        *reinterpret_cast<u32x4*>(s_q + row * Lay::QSTR + col * 8) = v;
-      }
-    }
-    __syncthreads();
     float beta = 0.f;  // ALiBi slope of this lane's head in raw-score units
-    if constexpr (ALIBI) beta = l32 < nh ? p.alibi[hbase + l32] * kLog2e / c : 0.f;
+    if constexpr (ALIBI) beta = l32 < cur.nh ? p.alibi[cur.hbase + l32] * kLog2e / c : 0.f;
+
+    // Each tile's K (V) registers are refilled as soon as QK^T (PV) has consumed them:
+    // with this wave's next tile of the segment, or after its last one with its first tile
+    // of the next segment.
     auto compute_tile = [&](TileRegs& r, int tt, bool more) {
-      const int j0 = (ft + tt) * DC_TILE;
+      const int j0 = (cur.ft + tt) * DC_TILE;
       f32x16 s = zero16();
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         const u32x4 qv = *reinterpret_cast<const u32x4*>(s_q + l32 * Lay::QSTR + ks * 16 + hh * 8);
         s = mfma_bf16_32x32x16(as_bf16x8(r.kf[ks]), as_bf16x8(qv), s);
       }
-      if (more) load_k(r, tt + DC_WAVES);  // K registers are free again: fetch the next tile
+      if (more)
+        load_k(r, cur, tt + DC_WAVES);
+      else if (pre_next)
+        load_k_from(r, rk_next);
       if constexpr (ALIBI) {  // the query sits at L_b - 1: bias -slope * (L_b - 1 - j)
-        const float dq = (float)(Lb - 1 - j0 - 4 * hh);
+        const float dq = (float)(cur.Lb - 1 - j0 - 4 * hh);
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr)
           s[rr] = fmaf(-beta, dq - (float)(8 * (rr >> 2) + (rr & 3)), s[rr]);
       }
-      const bool need_mask = j0 + DC_TILE > Lb || j0 < klo;
+      const bool need_mask = j0 + DC_TILE > cur.Lb || j0 < cur.klo;
       if (need_mask) {
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
           const int j = j0 + 8 * (rr >> 2) + 4 * hh + (rr & 3);
-          if (j >= Lb || j < klo) s[rr] = -INFINITY;
+          if (j >= cur.Lb || j < cur.klo) s[rr] = -INFINITY;
         }
       }
       float mx = -INFINITY;
@@ -397,13 +458,24 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_split_kernel(DecodeParam
           oacc[cc] = mfma_bf16_32x32x16(as_bf16x8(a), pb, oacc[cc]);
         }
       }
-      if (more) load_v(r, tt + DC_WAVES);  // V registers are free again
+      if (more)
+        load_v(r, cur, tt + DC_WAVES);  // V registers are free again
+      else if (pre_next)
+        load_v_from(r, rv_next);
     };
 
-    // The wave's tiles are ta + wave, ta + wave + DC_WAVES, ...; each tile's K (V)
-    // registers are refilled with the next tile's rows as soon as QK^T (PV) has consumed
-    // them.
-    for (int tt = ta + wave; tt < te; tt += DC_WAVES) compute_tile(r0, tt, tt + DC_WAVES < te);
+    // The wave's tiles of the segment are ta + wave, ta + wave + DC_WAVES, ...
+    for (int tt = cur.ta + wave; tt < cur.te; tt += DC_WAVES)
+      compute_tile(r0, tt, tt + DC_WAVES < cur.te);
+    if (cur.ta + wave >= cur.te && pre_next) {  // no tile here: request the next one now
+      load_k_from(r0, rk_next);
+      load_v_from(r0, rv_next);
+    }
+    // The next segment (b and bstart move on to it); its Q is requested before the merge
+    // and stored after it.
+    Seg nxt;
+    const bool has_next = find_seg(cur.next_t, b, bstart, nxt);
+    const u32x4 q_next = has_next ? load_q(nxt) : zero_u32x4();
 
     // Merge the waves' running states through LDS.
     const float l_tot = pair_sum(l_run);
@@ -443,7 +515,7 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_split_kernel(DecodeParam
       }
       const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
       const float lse_v = lsum > 0.f ? M * p.scale_abs + logf(lsum) : -INFINITY;
-      if (n < nh) {
+      if (n < cur.nh) {
         float val[CPT];
 #pragma unroll
         for (int dd = 0; dd < CPT; ++dd) val[dd] = 0.f;
@@ -458,8 +530,9 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_split_kernel(DecodeParam
           }
 #pragma unroll
         for (int dd = 0; dd < CPT; ++dd) val[dd] *= inv;
-        if (ta == 0 && te == Tb) {
-          uint16_t* orow = static_cast<uint16_t*>(p.o) + ((size_t)b * p.Hq + hbase + n) * D + dseg;
+        if (cur.ta == 0 && cur.te == cur.Tb) {
+          uint16_t* orow =
+              static_cast<uint16_t*>(p.o) + ((size_t)cur.b * p.Hq + cur.hbase + n) * D + dseg;
 #pragma unroll
           for (int q4 = 0; q4 < CPT / 4; ++q4) {
             u32x2 w2;
@@ -467,9 +540,9 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_split_kernel(DecodeParam
             w2[1] = pack_bf16x2(val[4 * q4 + 2], val[4 * q4 + 3]);
             *reinterpret_cast<u32x2*>(orow + 4 * q4) = w2;
           }
-          if (p.lse && (tid % SEGS) == 0) p.lse[(size_t)b * p.Hq + hbase + n] = lse_v;
+          if (p.lse && (tid % SEGS) == 0) p.lse[(size_t)cur.b * p.Hq + cur.hbase + n] = lse_v;
         } else {
-          const size_t slot = (size_t)w + u;
+          const size_t slot = (size_t)w + cur.u;
           float* dst = p.ws_o + (slot * 32 + n) * D + dseg;
 #pragma unroll
           for (int q4 = 0; q4 < CPT / 4; ++q4) {
@@ -482,8 +555,11 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_split_kernel(DecodeParam
         }
       }
     }
-    __syncthreads();  // LDS is reused by the next segment
-    t = ustart + te;
+    __syncthreads();  // the merge area and Q are free for the next segment
+    if (!has_next) break;
+    store_q(q_next);
+    __syncthreads();
+    cur = nxt;
   }
 }
 
@@ -567,8 +643,7 @@ __global__ __launch_bounds__(CB_THREADS) void decode_combine_kernel(DecodeParams
 template <int D, bool ALIBI, bool PAGED>
 hipError_t launch_d(const DecodeParams& p, bool need_combine, hipStream_t stream) {
   using Lay = DcLayout<D>;
-  const size_t lds = Lay::Q_BYTES + (Lay::O_FLOATS + 2 * DC_WAVES * 32) * sizeof(float) +
-                     (DC_WAVES + 4) * sizeof(long long);
+  const size_t lds = Lay::LDS;
   auto kern = decode_split_kernel<D, ALIBI, PAGED>;
   static KernelSetup setup;  // per device: LDS attribute set
   int dev = 0, cus = 0, per_cu = 1;
