@@ -16,12 +16,14 @@
 //     a normalised fp32 partial and its LSE to slot (w + u) (w and u never both
 //     decrease along the tile order, so w + u is unique), and the combine kernel
 //     merges a unit's partials in workgroup order with weights exp(lse_s - max).
-// Inside a workgroup the 8 waves take the segment's tiles round-robin and merge
-// their running (max, sum, O) through LDS.
+// Inside a workgroup the 8 waves take each segment's tiles (the part of one unit inside
+// the share) round-robin and merge their running (max, sum, O) through LDS. A wave
+// requests its first tile of the next segment, and the workgroup that segment's Q,
+// before the current segment's merge, so a share spanning several units streams on.
 //
 // Per 32-key tile, per wave (lane l: query l % 32 of the block, key half l / 32):
 //   S^T = K Q^T   (d/16) MFMA 32x32x16; K rows come straight from HBM as the A
-//                 operand (16 bytes per lane), Q^T stays in VGPRs;
+//                 operand (16 bytes per lane), Q^T is read back from LDS;
 //   online softmax over the 32 keys (running max / running sum);
 //   O^T += V^T P^T  2 x (d/32) MFMA; each lane loads d/32 consecutive values of 8
 //                 keys (one full row per 32 lanes, coalesced), and byte permutes
@@ -493,7 +495,8 @@ __global__ __launch_bounds__(DC_THREADS, 2) void decode_split_kernel(DecodeParam
             u32x4{__float_as_uint(oacc[0][r]), __float_as_uint(oacc[1][r]),
                   __float_as_uint(oacc[2][r]), __float_as_uint(oacc[3][r])};
       } else {
-        *reinterpret_cast<u32x2*>(dst) = u32x2{__float_as_uint(oacc[0][r]), __float_as_uint(oacc[1][r])};
+        *reinterpret_cast<u32x2*>(dst) =
+            u32x2{__float_as_uint(oacc[0][r]), __float_as_uint(oacc[1][r])};
       }
     }
     __syncthreads();

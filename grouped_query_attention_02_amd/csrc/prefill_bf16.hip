@@ -21,10 +21,10 @@
 // 168 for d = 128 without ALiBi) so that several waves share each SIMD (four, or three for
 // d = 128; two for d = 128 with ALiBi) and the hardware overlaps one wave's matrix
 // products with another wave's softmax. K/V tiles stream from HBM/L2 straight into an LDS
-// ring (4 slots, 3 with three workgroups per CU), RING - 1 tiles ahead of their use. The exponent offset is a row
-// max that is raised only when a tile's weights would exceed 2^32, so the O rescale is
-// rare; every term of a row always shares one offset, so the normalised result is
-// unchanged. The result equals textbook softmax(scale Q K^T) V
+// ring (4 slots, 3 with three workgroups per CU), RING - 1 tiles ahead of their use. The
+// exponent offset is a row max that is raised only when a tile's weights would exceed
+// 2^32, so the O rescale is rare; every term of a row always shares one offset, so the
+// normalised result is unchanged. The result equals textbook softmax(scale Q K^T) V
 // over the valid keys (aifullclass.xyz BERT self-attention article, LowRankSelfAttention
 // example; FlashAttention page FAQ: the computed result is mathematically the same).
 //

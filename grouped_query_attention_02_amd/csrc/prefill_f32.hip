@@ -20,7 +20,8 @@ constexpr int PF32_BN = 32;
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(PF32_THREADS) void prefill_f32_kernel(PrefillParams p) {
-  constexpr int KSTR = D + 2;  // K rows: lanes read one column of 32 rows -> stride = 2 mod 64 banks
+  // K rows: lanes read one column of 32 rows -> stride = 2 mod 64 banks
+  constexpr int KSTR = D + 2;
   constexpr int VSTR = D + 8;  // V rows: the two lane halves read rows 4 apart -> 32-bank offset
   __shared__ float ks_[PF32_BN * KSTR];
   __shared__ __attribute__((aligned(16))) float vs_[PF32_BN * VSTR];
@@ -122,7 +123,8 @@ __global__ __launch_bounds__(PF32_THREADS) void prefill_f32_kernel(PrefillParams
 
     f32x16 s = zero16();
 #pragma unroll
-    for (int ks = 0; ks < D / 2; ++ks) s = mfma_f32_32x32x2(ks_[l32 * KSTR + 2 * ks + hh], qf[ks], s);
+    for (int ks = 0; ks < D / 2; ++ks)
+      s = mfma_f32_32x32x2(ks_[l32 * KSTR + 2 * ks + hh], qf[ks], s);
 
     if (p.alibi) {
 #pragma unroll
