@@ -57,13 +57,17 @@ def _lse_err(gpu_lse, ref_lse):
 
 
 def _run_prefill_full(oracle_mod, q, k, v, seqlens, causal, scale, dtype):
+    """Max O error over the plain call and the LSE-returning call (different kernel
+    instantiations), and the LSE error."""
     dev = "cuda"
     lens_d = None if seqlens is None else torch.as_tensor(seqlens, dtype=torch.int32).to(dev)
-    o, lse = gqa.prefill(q.to(dev), k.to(dev), v.to(dev), causal=causal, softmax_scale=scale,
-                         seqlens=lens_d, return_lse=True)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o_plain = gqa.prefill(qd, kd, vd, causal=causal, softmax_scale=scale, seqlens=lens_d)
+    o, lse = gqa.prefill(qd, kd, vd, causal=causal, softmax_scale=scale, seqlens=lens_d,
+                         return_lse=True)
     torch.cuda.synchronize()
     ref_o, ref_l = oracle_mod.prefill(q, k, v, scale=scale, causal=causal, seqlens=seqlens)
-    return _max_err(o, ref_o), _lse_err(lse, ref_l)
+    return max(_max_err(o, ref_o), _max_err(o_plain, ref_o)), _lse_err(lse, ref_l)
 
 
 def test_tiny_f32_prefill_full(oracle_mod):

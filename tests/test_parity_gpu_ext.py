@@ -80,14 +80,17 @@ def test_prefill_window_alibi(oracle_mod, dtype, d, window, alibi, causal):
     scale = 1 / math.sqrt(d)
     for lens in (None, [150, 3, 77]):
         ld = None if lens is None else torch.tensor(lens, dtype=torch.int32, device="cuda")
+        o_plain = gqa.prefill(q.cuda(), k.cuda(), v.cuda(), causal=causal, softmax_scale=scale,
+                              seqlens=ld, window=window, alibi_slopes=slopes)
         o, lse = gqa.prefill(q.cuda(), k.cuda(), v.cuda(), causal=causal, softmax_scale=scale,
                              seqlens=ld, window=window, alibi_slopes=slopes, return_lse=True)
         torch.cuda.synchronize()
         ro, rl = oracle_mod.prefill(q, k, v, scale=scale, causal=causal, seqlens=lens,
                                     window=window, alibi_slopes=slopes)
+        e_plain, _ = _errs(o_plain, lse, ro, rl)
         e, le = _errs(o, lse, ro, rl)
-        _say(f"  lens={lens} max_abs_err={e:.3e} lse_err={le:.3e}")
-        assert e <= TOL[dtype] and le <= LSE_TOL[dtype]
+        _say(f"  lens={lens} max_abs_err={e_plain:.3e} (with LSE {e:.3e}) lse_err={le:.3e}")
+        assert e_plain <= TOL[dtype] and e <= TOL[dtype] and le <= LSE_TOL[dtype]
 
 
 NEG_CASES = [(dtype, d, w, a, c) for dtype in (torch.bfloat16, torch.float32)
