@@ -16,9 +16,10 @@
  *   - All array pointers are DEVICE pointers into memory the caller owns. The
  *     library never allocates or frees memory and keeps no pointer after a call
  *     returns. The only state it keeps between calls is set up once per device,
- *     on the first call on that device: the compute-unit count, and for each
- *     kernel its dynamic-LDS attribute and how many of its workgroups a compute
- *     unit holds.
+ *     on the first call on that device: the compute-unit count, for each kernel
+ *     its dynamic-LDS attribute and how many of its workgroups a compute unit
+ *     holds, and the device address of gqa_decode_noalloc's static scratch array
+ *     (part of the library's device code, not an allocation).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
  *     and the call returns right after the enqueue. No call synchronises the
  *     host or reads device memory from the host.
@@ -86,8 +87,10 @@ const char *gqa_status_string(int status);
  *                  j <= i (and j < seqlens[b]).
  *   stream         hipStream_t or NULL.
  * Returns GQA_OK, GQA_ERR_INVALID_ARG (B, S, Hq, Hkv <= 0, Hq % Hkv != 0,
- * NULL q/k/v/o, misaligned base), GQA_ERR_UNSUPPORTED (dtype or d) or
- * GQA_ERR_HIP.
+ * NULL q/k/v/o, misaligned base, a non-finite scale, causal not 0 or 1, or a
+ * problem whose row or workgroup counts overflow the kernels' 32-bit indices),
+ * GQA_ERR_UNSUPPORTED (dtype, d, or a bf16 problem whose K or V rows of one
+ * sequence span more than 2^31 - 1 bytes: S x Hkv x d x 2) or GQA_ERR_HIP.
  */
 int gqa_prefill(int dtype, const void *q, const void *k, const void *v, void *o, float *lse,
                 const int32_t *seqlens, int B, int S, int Hq, int Hkv, int d,
