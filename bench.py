@@ -23,6 +23,7 @@ time over the timed steps; `achieved` uses the mean, as the rocprofv3 --stats su
     python bench.py [--steps K] [--warmup W] [--settle-s S] [--no-cpu-baseline] [--no-extra]
                     [--no-probes] [--no-seeds]
     python bench.py --only WORKLOAD --steps K      (work for rocprofv3 runs: flush + call, K times)
+    python bench.py --power SECONDS   (power and clock under sustained load, per workload)
     python bench.py --summarize-kernels DIR | --summarize-pmc DIR
     python bench.py --traffic-summary WORKLOAD DIR_FETCH DIR_WRITE DIR_COPY_FETCH DIR_COPY_WRITE
 """
@@ -49,6 +50,7 @@ HEADLINE_PREFILL = "llama_causal_prefill"
 HEADLINE_DECODE = "gqa_decode_8k"
 FLUSH_BYTES = 768 << 20
 COPY_BYTES = 256 << 20
+GEMM_N = 8192
 CSRC = os.path.join(ROOT, "grouped_query_attention_02_amd", "csrc")
 
 # Kernels each workload launches (names as in rocprofv3 traces) and the sources they are built
@@ -198,6 +200,8 @@ class Case:
             key = "mfma_bf16_tflops" if self.bound == "mfma" else "hbm_read_gbps"
             if self.bound == "hbm" or w.dtype == "bf16":
                 b["frac_of_achievable"] = round(ach / achievable[key], 4)
+            if self.bound == "mfma" and w.dtype == "bf16" and achievable.get("gemm_bf16_tflops"):
+                b["frac_of_gemm"] = round(ach / achievable["gemm_bf16_tflops"], 4)
         if w.kind == "prefill":
             b["sum_key_len"] = None if self.lens_host is None else sum(self.lens_host)
         else:
@@ -663,8 +667,136 @@ def _achievable(dev) -> dict:
         gbps = max(gbps, nbytes / (best(rd, 5) * 1e-3) / 1e9)
     del buf, out
     torch.cuda.empty_cache()
+    gemm = _gemm_reference(dev, best)
     return {"mfma_bf16_tflops": round(tflops, 1), "hbm_read_gbps": round(gbps, 1),
-            "source": "probes/probes.hip: back-to-back bf16 MFMA; 4 GiB streaming read"}
+            "gemm_bf16_tflops": round(gemm, 1),
+            "source": "probes/probes.hip: back-to-back bf16 MFMA; 4 GiB streaming read; "
+                      f"gemm: torch.matmul (the vendor BLAS) on {GEMM_N}^3 bf16, a reference "
+                      "for the dense matrix-core rate reachable under the board's power limit"}
+
+
+def _gemm_reference(dev, best=None):
+    """TFLOP/s of a 2-D bf16 GEMM through torch.matmul (contiguous operands), the best of
+    several launches after one second of back-to-back calls: what the vendor's tuned GEMM
+    reaches on this board, to set the prefill fractions beside. Not part of the library."""
+    import torch
+    n = GEMM_N
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 1.0:
+        for _ in range(4):
+            torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+    ts = []
+    for _ in range(8):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.matmul(a, b, out=c)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del a, b, c
+    torch.cuda.empty_cache()
+    return 2.0 * n ** 3 / (min(ts) * 1e-3) / 1e12
+
+
+# ---------------------------------------------------------------- power and clock
+
+def _smi_sample():
+    """(socket power W, mean graphics clock over the XCDs in MHz) from one `amd-smi metric
+    -p -c` reading, or None where the tool or the fields are missing."""
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c"], capture_output=True, text=True,
+                           timeout=10)
+    except (OSError, subprocess.TimeoutExpired):
+        return None
+    pw = re.search(r"SOCKET_POWER: (\d+(?:\.\d+)?) W", r.stdout)
+    clks = [int(x) for x in re.findall(r"GFX_\d+:\s*\n\s*CLK: (\d+) MHz", r.stdout)]
+    if not pw or not clks:
+        return None
+    return float(pw.group(1)), statistics.mean(clks)
+
+
+def _power_cap():
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showmaxpower"], capture_output=True, text=True,
+                           timeout=20)
+    except (OSError, subprocess.TimeoutExpired):
+        return None
+    m = re.search(r"Max Graphics Package Power \(W\): ([\d.]+)", r.stdout)
+    return float(m.group(1)) if m else None
+
+
+def _power(seconds, dev):
+    """Power and clock under sustained load: each headline workload, then the bf16 GEMM
+    reference, called back to back (no flush) for `seconds` while a thread samples socket
+    power and graphics clock; one JSON line with, per row, the rate and the medians of the
+    samples taken after the first second."""
+    import threading
+    import torch
+    import workloads as W
+    cap = _power_cap()
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            s = _smi_sample()
+            if s:
+                samples.append((time.time(), *s))
+            time.sleep(0.05)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    rows = {}
+
+    def sustain(name, call, ncopies, work, unit):
+        for i in range(4):
+            call(i)
+        torch.cuda.synchronize()
+        t0, k = time.time(), 0
+        while time.time() - t0 < seconds:
+            for _ in range(8):
+                call(k % ncopies)
+                k += 1
+            torch.cuda.synchronize()
+        t1 = time.time()
+        sel = [x for x in samples if t0 + 1.0 <= x[0] <= t1]
+        scale = 1e12 if unit == "TFLOP/s" else 1e9
+        rows[name] = {
+            "rate": round(work * k / (t1 - t0) / scale, 1), "unit": unit,
+            "us_per_call": round((t1 - t0) / k * 1e6, 2), "calls": k,
+            "power_w_median": statistics.median(x[1] for x in sel) if sel else None,
+            "power_w_max": max(x[1] for x in sel) if sel else None,
+            "gfx_mhz_median": round(statistics.median(x[2] for x in sel)) if sel else None,
+            "samples": len(sel)}
+        _log(f"power: {name} {rows[name]}")
+        time.sleep(2.0)
+
+    for name in (HEADLINE_PREFILL, "bert_base_prefill", HEADLINE_DECODE, "mqa_ragged_decode"):
+        n = 2 if name == HEADLINE_DECODE else 4
+        c = Case(W.WORKLOADS[name], dev, n)
+        sustain(name, c.run, n, c.work, c.unit)
+        del c
+        torch.cuda.empty_cache()
+    n = GEMM_N
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    out = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    sustain(f"gemm_bf16_{n}", lambda i: torch.matmul(a, b, out=out), 1, 2.0 * n ** 3,
+            "TFLOP/s")
+    stop.set()
+    th.join()
+    print(json.dumps({"power_cap_w": cap, "seconds_per_row": seconds,
+                      "method": "calls back to back without the flush; amd-smi metric -p -c "
+                                "sampled in a thread; medians over samples after the first "
+                                "second", "rows": rows}), flush=True)
+    return 0
 
 
 # ---------------------------------------------------------------- profiling runs
@@ -705,6 +837,8 @@ def main(argv=None):
                     help="skip the achievable-peak microbenchmarks (achievable = null)")
     ap.add_argument("--no-seeds", action="store_true", help="skip the extra-seed runs")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--power", type=float, metavar="SECONDS",
+                    help="power and clock under sustained load, SECONDS per row, then exit")
     ap.add_argument("--only", choices=list(STEP_ORDER) + ["copy"],
                     help="profiling run: execute just this work --steps times and exit")
     ap.add_argument("--summarize-kernels", metavar="DIR")
@@ -737,6 +871,8 @@ def main(argv=None):
     _log(f"device {torch.cuda.get_device_name(0)}")
     if args.only:
         return _only(args.only, args.steps, dev)
+    if args.power:
+        return _power(args.power, dev)
 
     flush = Flusher(dev)
     cases = {}
@@ -792,7 +928,8 @@ def main(argv=None):
     if not args.no_probes:
         ach = _achievable(dev)
         _log(f"achievable: {ach['mfma_bf16_tflops']} TFLOP/s bf16 MFMA, "
-             f"{ach['hbm_read_gbps']} GB/s HBM read")
+             f"{ach['hbm_read_gbps']} GB/s HBM read, {ach['gemm_bf16_tflops']} TFLOP/s "
+             "bf16 GEMM")
     blocks = {name: cases[name].block(ach) for name in STEP_ORDER}
     for name, b in blocks.items():
         _log(f"{name}: mean {b['us_mean']:.2f} us median {b['us_median']:.2f} us -> "
