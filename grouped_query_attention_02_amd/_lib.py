@@ -4,6 +4,7 @@ from __future__ import annotations
 import ctypes
 import os
 import re
+import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libgqa.so")
@@ -39,12 +40,26 @@ def header_functions():
 LIBRARY_ENV = "GQA_LIBRARY_PATH"
 
 
+def _torch_runtime_first():
+    """torch ships its own HIP runtime under the soname this library links
+    (libamdhip64.so.7), and whichever copy a process loads first serves every library in it.
+    When torch is installed it is imported before the library, so that torch's own libraries
+    find the runtime they were built with (loaded the other way round, torch's first device
+    allocation and the library's launches fail with no-device and out-of-memory errors)."""
+    if "torch" in sys.modules:
+        return
+    import importlib.util
+    if importlib.util.find_spec("torch") is not None:
+        import torch  # noqa: F401
+
+
 def load():
     """Load libgqa.so from the package directory; raise if it has not been built."""
     global _lib
     if _lib is not None:
         return _lib
     path = os.environ.get(LIBRARY_ENV) or LIB_PATH
+    _torch_runtime_first()
     if not os.path.exists(path):
         raise RuntimeError(
             f"{path} is missing: build it with `python -m grouped_query_attention_02_amd.build` "

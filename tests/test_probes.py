@@ -1,5 +1,5 @@
 """The microbenchmarks bench.py compares its rates with (libgqa_probes.so): the library
-exports its three functions, the FLOP count is the stated formula, and on a GPU the read
+exports its four functions, the FLOP count is the stated formula, and on a GPU the read
 probe folds every 16-byte chunk exactly once (checked bit for bit against the CPU)."""
 import ctypes
 import os
@@ -14,23 +14,27 @@ from grouped_query_attention_02_amd import build as gbuild
 def probes(built_lib):
     if not os.path.exists(gbuild.PROBES_LIB):
         gbuild.build()
+    import torch  # noqa: F401  (torch's HIP runtime first; see _lib.load)
     lib = ctypes.CDLL(gbuild.PROBES_LIB, mode=ctypes.RTLD_LOCAL)
     lib.gqa_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
     lib.gqa_probe_mfma_flops.restype = ctypes.c_double
     lib.gqa_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                         ctypes.c_void_p]
+    lib.gqa_probe_mfma_bf16_rand.argtypes = lib.gqa_probe_mfma_bf16.argtypes
     lib.gqa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                    ctypes.c_int, ctypes.c_void_p]
     return lib
 
 
 def test_probe_exports_and_flop_count(probes):
-    for n in ("gqa_probe_mfma_bf16", "gqa_probe_read", "gqa_probe_mfma_flops"):
+    for n in ("gqa_probe_mfma_bf16", "gqa_probe_mfma_bf16_rand", "gqa_probe_read",
+              "gqa_probe_mfma_flops"):
         assert getattr(probes, n) is not None
     # blocks x 4 waves x iters x 4 chains x (2 x 32 x 32 x 16)
     assert probes.gqa_probe_mfma_flops(3, 5) == 3 * 4 * 5 * 4 * 2 * 32 * 32 * 16
     # invalid arguments are refused before any launch
     assert probes.gqa_probe_mfma_bf16(0, 1, None, None) != 0
+    assert probes.gqa_probe_mfma_bf16_rand(1, 6, None, None) != 0   # iters not a multiple of 4
     assert probes.gqa_probe_read(None, 16, None, 1, None) != 0
 
 
@@ -58,3 +62,13 @@ def test_mfma_probe_runs(probes):
     assert probes.gqa_probe_mfma_bf16(2, 10, out.data_ptr(), stream) == 0
     torch.cuda.synchronize()
     assert torch.isfinite(out).all()
+
+
+@pytest.mark.gpu
+def test_mfma_probe_random_operands_runs(probes):
+    import torch
+    out = torch.full((2 * 256,), float("nan"), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    assert probes.gqa_probe_mfma_bf16_rand(2, 8, out.data_ptr(), stream) == 0
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all() and (out != 0).any()
