@@ -200,8 +200,11 @@ class Case:
             key = "mfma_bf16_tflops" if self.bound == "mfma" else "hbm_read_gbps"
             if self.bound == "hbm" or w.dtype == "bf16":
                 b["frac_of_achievable"] = round(ach / achievable[key], 4)
-            if self.bound == "mfma" and w.dtype == "bf16" and achievable.get("gemm_bf16_tflops"):
-                b["frac_of_gemm"] = round(ach / achievable["gemm_bf16_tflops"], 4)
+            if self.bound == "mfma" and w.dtype == "bf16":
+                for k, f in (("mfma_bf16_random_operands_tflops", "frac_of_mfma_random_operands"),
+                             ("gemm_bf16_tflops", "frac_of_gemm")):
+                    if achievable.get(k):
+                        b[f] = round(ach / achievable[k], 4)
         if w.kind == "prefill":
             b["sum_key_len"] = None if self.lens_host is None else sum(self.lens_host)
         else:
@@ -652,6 +655,19 @@ def _achievable(dev) -> dict:
     best(mfma, 3)
     ms = best(mfma, 8)
     tflops = lib.gqa_probe_mfma_flops(blocks, iters) / (ms * 1e-3) / 1e12
+    # The same products on random operands (the multipliers toggle as on real data), after
+    # a second of back-to-back launches so that the clock has settled at its power limit.
+    lib.gqa_probe_mfma_bf16_rand.argtypes = lib.gqa_probe_mfma_bf16.argtypes
+
+    def mfma_rand():
+        return lib.gqa_probe_mfma_bf16_rand(blocks, iters, out.data_ptr(), stream)
+
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 1.0:
+        for _ in range(8):
+            mfma_rand()
+        torch.cuda.synchronize()
+    rand_tflops = lib.gqa_probe_mfma_flops(blocks, iters) / (best(mfma_rand, 8) * 1e-3) / 1e12
     nbytes = 4 << 30
     buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     buf.zero_()
@@ -669,8 +685,10 @@ def _achievable(dev) -> dict:
     torch.cuda.empty_cache()
     gemm = _gemm_reference(dev, best)
     return {"mfma_bf16_tflops": round(tflops, 1), "hbm_read_gbps": round(gbps, 1),
+            "mfma_bf16_random_operands_tflops": round(rand_tflops, 1),
             "gemm_bf16_tflops": round(gemm, 1),
-            "source": "probes/probes.hip: back-to-back bf16 MFMA; 4 GiB streaming read; "
+            "source": "probes/probes.hip: back-to-back bf16 MFMA on fixed operands, and on "
+                      "random operands after 1 s at the power limit; 4 GiB streaming read; "
                       f"gemm: torch.matmul (the vendor BLAS) on {GEMM_N}^3 bf16, a reference "
                       "for the dense matrix-core rate reachable under the board's power limit"}
 
@@ -735,9 +753,9 @@ def _power_cap():
 
 def _power(seconds, dev):
     """Power and clock under sustained load: each headline workload, then the bf16 GEMM
-    reference, called back to back (no flush) for `seconds` while a thread samples socket
-    power and graphics clock; one JSON line with, per row, the rate and the medians of the
-    samples taken after the first second."""
+    reference and the matrix-core probe, called back to back (no flush) for `seconds` while a
+    thread samples socket power and graphics clock; one JSON line with, per row, the rate and
+    the medians of the samples taken after the first second."""
     import threading
     import torch
     import workloads as W
@@ -790,6 +808,31 @@ def _power(seconds, dev):
     out = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
     sustain(f"gemm_bf16_{n}", lambda i: torch.matmul(a, b, out=out), 1, 2.0 * n ** 3,
             "TFLOP/s")
+    del a, b, out
+    torch.cuda.empty_cache()
+    # The matrix-core probe alone (no memory traffic): what the matrix cores sustain at the cap.
+    import ctypes
+    from grouped_query_attention_02_amd import build as gbuild
+    lib = ctypes.CDLL(gbuild.PROBES_LIB, mode=ctypes.RTLD_LOCAL)
+    lib.gqa_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.gqa_probe_mfma_flops.restype = ctypes.c_double
+    lib.gqa_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    blocks, iters = 4 * torch.cuda.get_device_properties(dev).multi_processor_count, 1000
+    pout = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def probe(i):
+        if lib.gqa_probe_mfma_bf16(blocks, iters, pout.data_ptr(), stream) != 0:
+            raise RuntimeError("probe launch failed")
+    sustain("mfma_probe_bf16", probe, 1, lib.gqa_probe_mfma_flops(blocks, iters), "TFLOP/s")
+    lib.gqa_probe_mfma_bf16_rand.argtypes = lib.gqa_probe_mfma_bf16.argtypes
+
+    def probe_rand(i):
+        if lib.gqa_probe_mfma_bf16_rand(blocks, iters, pout.data_ptr(), stream) != 0:
+            raise RuntimeError("probe launch failed")
+    sustain("mfma_probe_bf16_random_operands", probe_rand, 1,
+            lib.gqa_probe_mfma_flops(blocks, iters), "TFLOP/s")
     stop.set()
     th.join()
     print(json.dumps({"power_cap_w": cap, "seconds_per_row": seconds,
@@ -927,7 +970,8 @@ def main(argv=None):
     ach = None
     if not args.no_probes:
         ach = _achievable(dev)
-        _log(f"achievable: {ach['mfma_bf16_tflops']} TFLOP/s bf16 MFMA, "
+        _log(f"achievable: {ach['mfma_bf16_tflops']} TFLOP/s bf16 MFMA "
+             f"({ach['mfma_bf16_random_operands_tflops']} on random operands), "
              f"{ach['hbm_read_gbps']} GB/s HBM read, {ach['gemm_bf16_tflops']} TFLOP/s "
              "bf16 GEMM")
     blocks = {name: cases[name].block(ach) for name in STEP_ORDER}

@@ -4,6 +4,8 @@
 //   gqa_probe_mfma_bf16: back-to-back v_mfma_f32_32x32x16_bf16 with four independent
 //     accumulator chains per wave; one launch does blocks x 4 waves x iters x 4 products
 //     of 32 x 32 x 16 (2 x 16384 FLOP each).
+//   gqa_probe_mfma_bf16_rand: the same products on random operands cycled over four register
+//     sets (the multipliers toggle as on real data; the fixed operands above barely do).
 //   gqa_probe_read: every 16-byte chunk of a buffer read once (grid-stride), XOR-folded
 //     so nothing is optimised away; the achievable HBM read rate for a buffer far larger
 //     than the last-level cache.
@@ -44,6 +46,59 @@ __global__ __launch_bounds__(256, 4) void mfma_probe(int iters, float* out) {
   out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// Random-operand variant: four sets of A and B operands with random bf16 values (sign and
+// mantissa from a hash of the lane, magnitudes in [0.5, 2)), cycled so that consecutive
+// products see different data, as the multipliers do on real inputs.
+__device__ unsigned mix32(unsigned x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+
+__device__ unsigned rand_bf16x2(unsigned seed) {
+  const unsigned h = mix32(seed);
+  const unsigned lo = ((h & 1u) << 15) | ((126u + ((h >> 1) & 1u)) << 7) | ((h >> 2) & 0x7fu);
+  const unsigned hi = (((h >> 9) & 1u) << 15) | ((126u + ((h >> 10) & 1u)) << 7) | ((h >> 11) & 0x7fu);
+  return lo | (hi << 16);
+}
+
+constexpr int kSets = 4;
+
+__global__ __launch_bounds__(256, 4) void mfma_probe_rand(int iters, float* out) {
+  u32x4 a[kSets], b[kSets];
+  const unsigned t = blockIdx.x * blockDim.x + threadIdx.x;
+#pragma unroll
+  for (int s = 0; s < kSets; ++s)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[s][i] = rand_bf16x2(t * 64u + s * 8u + i);
+      b[s][i] = rand_bf16x2(t * 64u + s * 8u + 4u + i + 0x9e3779b9u);
+    }
+  f32x16 acc[kChains];
+#pragma unroll
+  for (int k = 0; k < kChains; ++k)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[k][r] = 0.f;
+  for (int it = 0; it < iters; it += kSets) {
+#pragma unroll
+    for (int u = 0; u < kSets; ++u)
+#pragma unroll
+      for (int k = 0; k < kChains; ++k)
+        acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, a[(u + k) % kSets]),
+            __builtin_bit_cast(bf16x8, b[(u + 2 * k + 1) % kSets]), acc[k], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < kChains; ++k)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[k][r];
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
 __global__ __launch_bounds__(256) void read_probe(const u32x4* buf, size_t n, unsigned* out) {
   u32x4 acc = {0u, 0u, 0u, 0u};
   const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -65,6 +120,15 @@ int gqa_probe_mfma_bf16(int blocks, int iters, float* out, void* stream) {
   if (blocks <= 0 || iters <= 0 || !out) return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(mfma_probe, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
                      iters, out);
+  return (int)hipGetLastError();
+}
+
+// As gqa_probe_mfma_bf16 with random operands cycled over four register sets; iters must be
+// a multiple of 4 (same FLOPs per launch as gqa_probe_mfma_flops gives).
+int gqa_probe_mfma_bf16_rand(int blocks, int iters, float* out, void* stream) {
+  if (blocks <= 0 || iters <= 0 || iters % kSets || !out) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(mfma_probe_rand, dim3(blocks), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), iters, out);
   return (int)hipGetLastError();
 }
 
