@@ -622,7 +622,8 @@ def _cpu_baseline(case, target_s: float):
 def _achievable(dev) -> dict:
     """Achievable peaks on this GPU from libgqa_probes.so: back-to-back bf16 32x32x16 MFMAs
     (four independent chains per wave, four waves per SIMD) and a read of a 4 GiB buffer
-    (16 x the last-level cache), each the best of several timed launches."""
+    (16 x the last-level cache) with plain and with non-temporal loads, each the best of
+    several timed launches."""
     import ctypes
     import torch
     from grouped_query_attention_02_amd import build as gbuild
@@ -632,6 +633,7 @@ def _achievable(dev) -> dict:
     lib.gqa_probe_mfma_flops.restype = ctypes.c_double
     lib.gqa_probe_mfma_bf16.argtypes = [i32, i32, vp, vp]
     lib.gqa_probe_read.argtypes = [vp, ctypes.c_size_t, vp, i32, vp]
+    lib.gqa_probe_read_nt.argtypes = lib.gqa_probe_read.argtypes
     stream = torch.cuda.current_stream().cuda_stream
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     blocks, iters = 4 * cus, 1000
@@ -671,24 +673,30 @@ def _achievable(dev) -> dict:
     nbytes = 4 << 30
     buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     buf.zero_()
-    gbps = 0.0
-    for per_cu in (4, 8, 16):
-        rblocks = per_cu * cus
-        rout = torch.empty(rblocks * 256, dtype=torch.int32, device=dev)
+    rates = {}
+    for name, fn in (("plain", lib.gqa_probe_read), ("nt", lib.gqa_probe_read_nt)):
+        g = 0.0
+        for per_cu in (4, 8, 16):
+            rblocks = per_cu * cus
+            rout = torch.empty(rblocks * 256, dtype=torch.int32, device=dev)
 
-        def rd():
-            return lib.gqa_probe_read(buf.data_ptr(), nbytes // 16, rout.data_ptr(), rblocks,
-                                      stream)
-        best(rd, 2)
-        gbps = max(gbps, nbytes / (best(rd, 5) * 1e-3) / 1e9)
+            def rd():
+                return fn(buf.data_ptr(), nbytes // 16, rout.data_ptr(), rblocks, stream)
+            best(rd, 2)
+            g = max(g, nbytes / (best(rd, 5) * 1e-3) / 1e9)
+        rates[name] = g
+    gbps = max(rates.values())
     del buf, out
     torch.cuda.empty_cache()
     gemm = _gemm_reference(dev, best)
     return {"mfma_bf16_tflops": round(tflops, 1), "hbm_read_gbps": round(gbps, 1),
+            "hbm_read_plain_gbps": round(rates["plain"], 1),
+            "hbm_read_nt_gbps": round(rates["nt"], 1),
             "mfma_bf16_random_operands_tflops": round(rand_tflops, 1),
             "gemm_bf16_tflops": round(gemm, 1),
             "source": "probes/probes.hip: back-to-back bf16 MFMA on fixed operands, and on "
-                      "random operands after 1 s at the power limit; 4 GiB streaming read; "
+                      "random operands after 1 s at the power limit; 4 GiB streaming read with "
+                      "plain and with non-temporal loads (hbm_read_gbps: the better); "
                       f"gemm: torch.matmul (the vendor BLAS) on {GEMM_N}^3 bf16, a reference "
                       "for the dense matrix-core rate reachable under the board's power limit"}
 

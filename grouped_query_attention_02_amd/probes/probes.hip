@@ -6,7 +6,7 @@
 //     of 32 x 32 x 16 (2 x 16384 FLOP each).
 //   gqa_probe_mfma_bf16_rand: the same products on random operands cycled over four register
 //     sets (the multipliers toggle as on real data; the fixed operands above barely do).
-//   gqa_probe_read: every 16-byte chunk of a buffer read once (grid-stride), XOR-folded
+//   gqa_probe_read / gqa_probe_read_nt: every 16-byte chunk of a buffer read once (grid-stride), XOR-folded
 //     so nothing is optimised away; the achievable HBM read rate for a buffer far larger
 //     than the last-level cache.
 #include <hip/hip_runtime.h>
@@ -106,6 +106,15 @@ __global__ __launch_bounds__(256) void read_probe(const u32x4* buf, size_t n, un
   out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 
+// The same read with non-temporal loads (`nt`: lines read once are not kept).
+__global__ __launch_bounds__(256) void read_probe_nt(const u32x4* buf, size_t n, unsigned* out) {
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    acc ^= __builtin_nontemporal_load(buf + i);
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
 }  // namespace
 
 extern "C" {
@@ -136,6 +145,14 @@ int gqa_probe_mfma_bf16_rand(int blocks, int iters, float* out, void* stream) {
 int gqa_probe_read(const void* buf, size_t n16, unsigned* out, int blocks, void* stream) {
   if (!buf || !out || blocks <= 0 || ((uintptr_t)buf & 15u)) return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(read_probe, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4*>(buf), n16, out);
+  return (int)hipGetLastError();
+}
+
+// As gqa_probe_read with non-temporal loads.
+int gqa_probe_read_nt(const void* buf, size_t n16, unsigned* out, int blocks, void* stream) {
+  if (!buf || !out || blocks <= 0 || ((uintptr_t)buf & 15u)) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(read_probe_nt, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
                      static_cast<const u32x4*>(buf), n16, out);
   return (int)hipGetLastError();
 }

@@ -1,5 +1,5 @@
 """The microbenchmarks bench.py compares its rates with (libgqa_probes.so): the library
-exports its four functions, the FLOP count is the stated formula, and on a GPU the read
+exports its five functions, the FLOP count is the stated formula, and on a GPU the read
 probe folds every 16-byte chunk exactly once (checked bit for bit against the CPU)."""
 import ctypes
 import os
@@ -23,12 +23,13 @@ def probes(built_lib):
     lib.gqa_probe_mfma_bf16_rand.argtypes = lib.gqa_probe_mfma_bf16.argtypes
     lib.gqa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                    ctypes.c_int, ctypes.c_void_p]
+    lib.gqa_probe_read_nt.argtypes = lib.gqa_probe_read.argtypes
     return lib
 
 
 def test_probe_exports_and_flop_count(probes):
     for n in ("gqa_probe_mfma_bf16", "gqa_probe_mfma_bf16_rand", "gqa_probe_read",
-              "gqa_probe_mfma_flops"):
+              "gqa_probe_read_nt", "gqa_probe_mfma_flops"):
         assert getattr(probes, n) is not None
     # blocks x 4 waves x iters x 4 chains x (2 x 32 x 32 x 16)
     assert probes.gqa_probe_mfma_flops(3, 5) == 3 * 4 * 5 * 4 * 2 * 32 * 32 * 16
@@ -36,6 +37,7 @@ def test_probe_exports_and_flop_count(probes):
     assert probes.gqa_probe_mfma_bf16(0, 1, None, None) != 0
     assert probes.gqa_probe_mfma_bf16_rand(1, 6, None, None) != 0   # iters not a multiple of 4
     assert probes.gqa_probe_read(None, 16, None, 1, None) != 0
+    assert probes.gqa_probe_read_nt(None, 16, None, 1, None) != 0
 
 
 @pytest.mark.gpu
@@ -47,11 +49,13 @@ def test_read_probe_folds_every_chunk(probes):
     buf = torch.from_numpy(host.view(np.int32)).cuda()
     out = torch.zeros(blocks * 256, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
-    assert probes.gqa_probe_read(buf.data_ptr(), n16, out.data_ptr(), blocks, stream) == 0
-    torch.cuda.synchronize()
-    got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
     want = np.bitwise_xor.reduce(host.reshape(-1))
-    assert got == want
+    for fn in (probes.gqa_probe_read, probes.gqa_probe_read_nt):
+        out.zero_()
+        assert fn(buf.data_ptr(), n16, out.data_ptr(), blocks, stream) == 0
+        torch.cuda.synchronize()
+        got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
+        assert got == want
 
 
 @pytest.mark.gpu
