@@ -335,6 +335,23 @@ def test_decode_many_sequences(oracle_mod, d, B):
         assert e <= 2e-2 and le <= BF16_DECODE_LSE_TOL
 
 
+def test_decode_long_context(oracle_mod):
+    """128k-key caches, one full and one ragged; with one split per unit a workgroup streams a
+    whole 131072-key unit (64 MiB of K and V) and no merge runs."""
+    B, Hq, Hkv, d, max_len = 2, 16, 2, 128, 131072
+    lens = [131072, 98765]
+    _say(f"case decode long context max_len={max_len} lens={lens}")
+    q = _rand((B, Hq, d), 4101, torch.bfloat16)
+    kc = _rand((B, Hkv, max_len, d), 4102, torch.bfloat16)
+    vc = _rand((B, Hkv, max_len, d), 4103, torch.bfloat16)
+    # scale 0.5: scores of std ~5.7, so a few of the 131072 keys dominate and O has values
+    # of order one (with 1/sqrt(d) the weights are spread thin and O is small)
+    for scale, splits in ((1 / math.sqrt(d), 0), (0.5, 0), (0.5, 1), (0.5, 5)):
+        e, le, _ = _run_decode_full(oracle_mod, q, kc, vc, lens, scale, splits)
+        _say(f"  scale={scale:.3f} splits={splits} max_abs_err={e:.3e} lse_err={le:.3e}")
+        assert e <= 2e-2 and le <= BF16_DECODE_LSE_TOL
+
+
 def test_decode_poisoned_cache_and_split_invariance(oracle_mod):
     """NaN/Inf past each length must not leak; every split count gives the oracle's answer."""
     B, Hq, Hkv, d, max_len = 5, 32, 1, 128, 2000
