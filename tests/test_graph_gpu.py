@@ -3,7 +3,8 @@ synchronises and enqueues only kernel launches on the caller's stream, so a whol
 (prefill and decode calls, the workspace decode and the allocation-free decode) can be
 captured once and replayed. Each replay runs on new inputs copied into the captured
 buffers, with eager calls and synchronisations between replays, and must give outputs
-bitwise equal to eager calls on the same inputs (the kernels are deterministic)."""
+bitwise equal to eager calls on the same inputs (the kernels are deterministic). A
+fresh process whose first library calls happen under capture replays them correctly too."""
 import sys
 
 import pytest
@@ -115,3 +116,47 @@ def test_step_replays_match_eager_calls():
         same = [torch.equal(a, b) for a, b in zip(got, want)]
         _say(f"  replay {rep}: outputs bitwise equal to eager calls: {same}")
         assert all(same)
+
+
+_COLD_CAPTURE = r'''
+import sys
+import torch
+import grouped_query_attention_02_amd as gqa
+dev = torch.device("cuda:0")
+g = torch.Generator().manual_seed(5)
+def rnd(shape):
+    return torch.randn(shape, generator=g).to(torch.bfloat16).to(dev)
+q, k, v = rnd((2, 200, 8, 128)), rnd((2, 200, 2, 128)), rnd((2, 200, 2, 128))
+dq, kc, vc = rnd((3, 16, 128)), rnd((3, 2, 900, 128)), rnd((3, 2, 900, 128))
+lens = torch.tensor([900, 5, 444], dtype=torch.int32, device=dev)
+o1, o2, o3 = torch.empty_like(q), torch.empty_like(dq), torch.empty_like(dq)
+ws = torch.empty(gqa.decode_workspace_bytes(3, 16, 2, 128, 900, 0), dtype=torch.uint8,
+                 device=dev)
+torch.cuda.synchronize()
+graph = torch.cuda.CUDAGraph()
+with torch.cuda.graph(graph):   # the library's first calls in this process
+    gqa.prefill(q, k, v, causal=True, out=o1)
+    gqa.decode(dq, kc, vc, lens, workspace=ws, out=o2)
+    gqa.decode_noalloc(dq, kc, vc, lens, o3)
+graph.replay()
+torch.cuda.synchronize()
+r1, r2 = gqa.prefill(q, k, v, causal=True), gqa.decode(dq, kc, vc, lens)
+torch.cuda.synchronize()
+ok = torch.equal(o1, r1) and torch.equal(o2, r2) and torch.equal(o3, r2)
+print("cold capture replay equals eager:", ok, flush=True)
+sys.exit(0 if ok else 1)
+'''
+
+
+def test_first_calls_captured_in_fresh_process():
+    """The per-device set-up done on a device's first call (CU count, kernel attributes,
+    occupancy, the scratch address) is allowed under stream capture: a fresh process whose
+    first library calls are inside a graph capture replays them correctly."""
+    import os
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, PYTHONPATH=root + os.pathsep + os.environ.get("PYTHONPATH", ""))
+    r = subprocess.run([sys.executable, "-c", _COLD_CAPTURE], cwd=root, env=env,
+                       capture_output=True, text=True, timeout=110)
+    _say(r.stdout.strip())
+    assert r.returncode == 0, r.stderr[-2000:]
